@@ -1,0 +1,155 @@
+"""fp64 CPU oracle for block-hybrid attention -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never touches it, and it never touches the product path.
+
+The arithmetic lives in ``hba_oracle.c`` (plain C, fp64, written from
+"Retrofitting Linear Attention into Diffusion Language Models", sections 2.2
+and 3.1).  This module only compiles that file with gcc and marshals numpy
+arrays to it.  Every array handed in is converted to contiguous fp64, which is
+exact for bf16 and fp32 inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "hba_oracle.c")
+_LIB = os.path.join(_HERE, "libhba_oracle.so")
+
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (host only, OpenMP over independent pairs)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib_handle = None
+
+
+def _lib():
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        lib.orc_threads.argtypes = [ctypes.c_int]
+        lib.orc_threads.restype = ctypes.c_int
+        lib.orc_feature_map.argtypes = [i64, i32, i32, i32, _f64p, _f64p, _f64p, ctypes.c_int]
+        lib.orc_commit.argtypes = [i32, i32, i32, i32, i32, _i32p, _f64p, _f64p, _f64p,
+                                   _f64p, _f64p, _i32p, ctypes.c_int]
+        lib.orc_step.argtypes = [i32, i32, i32, i32, i32, _f64p, _f64p, _f64p, _f64p, _f64p,
+                                 _f64p, _f64p, _i32p, _f64p, ctypes.c_int]
+        lib.orc_prefix_softmax.argtypes = [i32, i32, i32, i32, i32, _i32p, _f64p, _f64p, _f64p,
+                                           _f64p, _f64p, _f64p, ctypes.c_int]
+        for fn in (lib.orc_feature_map, lib.orc_commit, lib.orc_step, lib.orc_prefix_softmax):
+            fn.restype = ctypes.c_int
+        _lib_handle = lib
+    return _lib_handle
+
+
+def _f64(a) -> np.ndarray:
+    if hasattr(a, "detach"):  # torch tensor: widen exactly on the host
+        a = a.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _i32(a):
+    if a is None:
+        return None
+    if hasattr(a, "detach"):
+        a = a.detach().to("cpu").numpy()
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _p(a, t=_f64p):
+    return None if a is None else a.ctypes.data_as(t)
+
+
+def threads(nthreads: int = 0) -> int:
+    """Threads an oracle call with ``nthreads`` (0 = OpenMP default) uses."""
+    return int(_lib().orc_threads(nthreads))
+
+
+def feature_map(x, W, nthreads: int = 0) -> np.ndarray:
+    """phi = [softmax(xW), softmax(-xW)] per head.  x [n][H][d], W [H][d][F]
+    -> phi [n][H][2F] (section 3.1, Hedgehog feature map)."""
+    x, W = _f64(x), _f64(W)
+    n, H, d = x.shape
+    F = W.shape[2]
+    assert W.shape == (H, d, F)
+    phi = np.zeros((n, H, 2 * F))
+    rc = _lib().orc_feature_map(n, H, d, F, _p(x), _p(W), _p(phi), nthreads)
+    if rc:
+        raise OracleError(f"orc_feature_map rc={rc}")
+    return phi
+
+
+def commit(S_pool, Z_pool, k, v, W, n_valid=None, slot=None, nthreads: int = 0):
+    """Fold k, v [B][H][T][d] into the pool states in place (section 3.1,
+    state update).  Returns the (fp64) S_pool, Z_pool arrays it updated."""
+    S_pool, Z_pool = _f64(S_pool).copy(), _f64(Z_pool).copy()
+    k, v, W = _f64(k), _f64(v), _f64(W)
+    B, H, T, d = k.shape
+    F = W.shape[2]
+    assert v.shape == k.shape and W.shape == (H, d, F)
+    assert S_pool.shape[1:] == (H, 2 * F, d) and Z_pool.shape[1:] == (H, 2 * F)
+    nv, sl = _i32(n_valid), _i32(slot)
+    rc = _lib().orc_commit(B, H, T, d, F, _p(nv, _i32p), _p(k), _p(v), _p(W),
+                           _p(S_pool), _p(Z_pool), _p(sl, _i32p), nthreads)
+    if rc:
+        raise OracleError(f"orc_commit rc={rc}")
+    return S_pool, Z_pool
+
+
+def step(q, k, v, W, S_pool, Z_pool, gate=None, slot=None, nthreads: int = 0) -> np.ndarray:
+    """One block-hybrid denoising step; q, k, v [B][H][L][d] -> out [B][H][L][d]
+    (section 3.1: within-block softmax, linear readout, gated merge)."""
+    q, k, v, W = _f64(q), _f64(k), _f64(v), _f64(W)
+    S_pool, Z_pool = _f64(S_pool), _f64(Z_pool)
+    B, H, L, d = q.shape
+    F = W.shape[2]
+    assert k.shape == q.shape and v.shape == q.shape and W.shape == (H, d, F)
+    assert S_pool.shape[1:] == (H, 2 * F, d) and Z_pool.shape[1:] == (H, 2 * F)
+    g = None if gate is None else _f64(gate)
+    sl = _i32(slot)
+    out = np.zeros((B, H, L, d))
+    rc = _lib().orc_step(B, H, L, d, F, _p(q), _p(k), _p(v), _p(W), _p(g),
+                         _p(S_pool), _p(Z_pool), _p(sl, _i32p), _p(out), nthreads)
+    if rc:
+        raise OracleError(f"orc_step rc={rc}")
+    return out
+
+
+def prefix_softmax(q, k, v, Kc, Vc, prefix_len=None, nthreads: int = 0) -> np.ndarray:
+    """Full softmax attention of block queries over [prefix cache ; block]
+    (section 2.2, softmax attention): the comparator.  Kc, Vc [B][H][P][d]."""
+    q, k, v, Kc, Vc = _f64(q), _f64(k), _f64(v), _f64(Kc), _f64(Vc)
+    B, H, L, d = q.shape
+    P = Kc.shape[2]
+    assert Kc.shape == (B, H, P, d) and Vc.shape == Kc.shape
+    pl = _i32(prefix_len)
+    out = np.zeros((B, H, L, d))
+    rc = _lib().orc_prefix_softmax(B, H, L, d, P, _p(pl, _i32p), _p(q), _p(k), _p(v),
+                                   _p(Kc), _p(Vc), _p(out), nthreads)
+    if rc:
+        raise OracleError(f"orc_prefix_softmax rc={rc}")
+    return out

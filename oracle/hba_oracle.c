@@ -1,0 +1,251 @@
+/*
+ * hba_oracle.c -- plain fp64 CPU statement of block-hybrid attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the checker, not the product: only
+ * the tests, the smoke check and the benchmark's CPU-baseline leg may load it.
+ * It shares no code, header, table or helper with the HIP library; the two
+ * meet only in the seeded inputs the tests hand to both.
+ *
+ * Source of every formula: "Retrofitting Linear Attention into Diffusion
+ * Language Models" (arXiv 2608.06628), section 2.2 (softmax attention, linear
+ * attention Eq. 1 and its recurrent state) and section 3.1 (within-block
+ * softmax numerator/normaliser, Hedgehog feature map, the states S and Z and
+ * their per-block update, the linear readout, the gated shared-normaliser
+ * merge).  Each function below names the passage it writes out.
+ *
+ * Everything is fp64.  Inputs that are bf16 or fp32 on the device arrive here
+ * widened exactly to fp64 by the caller.  Loops run in the order the formulas
+ * are written; the only parallelism is an OpenMP split over independent
+ * (request, head) pairs, which does not change any element's arithmetic.
+ *
+ * Layouts (row-major, C order):
+ *   x, q, k, v, out   [B][H][L][d]        one block of L tokens per request
+ *   W                 [H][d][F]           u = x W  (W is d x F, per head)
+ *   gate              [H] or NULL         w = sigma(alpha); NULL means w = 1
+ *   S pool            [n_slots][H][2F][d] S = sum phi(k) v^T
+ *   Z pool            [n_slots][H][2F]    Z = sum phi(k)
+ *   slot              [B] or NULL         request -> pool slot; NULL means b
+ *   Kc, Vc            [B][H][P][d]        full prefix cache for the comparator
+ *
+ * Parity of each function is pinned by the CPU tests against closed forms,
+ * a hand-worked example, library softmax/SDPA and brute-force Eq. 1.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Largest |score| for which exp() of the unshifted score stays far from fp64
+ * overflow (exp(709) is the limit).  The step and comparator below use the
+ * unshifted definition, so they refuse inputs beyond it. */
+#define ORC_MAX_ABS_SCORE 700.0
+
+/* Hedgehog feature map for one row (section 3.1, feature-map definition):
+ *   u = x W,  phi(x) = [softmax(u), softmax(-u)]  in R^{2F}.
+ * softmax(u)_f = exp(u_f) / sum_g exp(u_g).  The exponent is shifted by
+ * max(u) (resp. max(-u) = -min(u)); the shift cancels between numerator and
+ * denominator, so this is the definition itself, safe for any finite u. */
+static void phi_row(int d, int F, const double *x, const double *W,
+                    double *u, double *phi) {
+    for (int f = 0; f < F; ++f) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += x[i] * W[(int64_t)i * F + f];
+        u[f] = acc;
+    }
+    double mx = u[0], mn = u[0];
+    for (int f = 1; f < F; ++f) {
+        if (u[f] > mx) mx = u[f];
+        if (u[f] < mn) mn = u[f];
+    }
+    double sp = 0.0, sn = 0.0;
+    for (int f = 0; f < F; ++f) {
+        sp += exp(u[f] - mx);
+        sn += exp(-u[f] + mn);
+    }
+    for (int f = 0; f < F; ++f) {
+        phi[f] = exp(u[f] - mx) / sp;
+        phi[F + f] = exp(-u[f] + mn) / sn;
+    }
+}
+
+static int threads_or_default(int nthreads) {
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/* Number of threads an OpenMP region with this request would use. */
+int orc_threads(int nthreads) { return threads_or_default(nthreads); }
+
+/* phi for n rows of x [n][H][d] with per-head W [H][d][F] -> phi [n][H][2F]. */
+int orc_feature_map(int64_t n, int H, int d, int F, const double *x,
+                    const double *W, double *phi, int nthreads) {
+    if (n < 0 || H <= 0 || d <= 0 || F <= 0) return 1;
+    int nt = threads_or_default(nthreads);
+    #pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t r = 0; r < n * H; ++r) {
+        int h = (int)(r % H);
+        double *u = (double *)malloc(sizeof(double) * F);
+        phi_row(d, F, x + r * d, W + (int64_t)h * d * F, u, phi + r * 2 * F);
+        free(u);
+    }
+    return 0;
+}
+
+/* State commit (section 3.1, per-block state update):
+ *   S_n = S_{n-1} + sum_{t in block} phi(k_t) v_t^T,
+ *   Z_n = Z_{n-1} + sum_{t in block} phi(k_t).
+ * Written token by token.  Request b folds its first n_valid[b] tokens
+ * (all T when n_valid is NULL) into pool slot slot[b] (b when NULL). */
+int orc_commit(int B, int H, int T, int d, int F, const int32_t *n_valid,
+               const double *k, const double *v, const double *W,
+               double *S_pool, double *Z_pool, const int32_t *slot,
+               int nthreads) {
+    if (B < 0 || H <= 0 || T < 0 || d <= 0 || F <= 0) return 1;
+    const int P2 = 2 * F;
+    int nt = threads_or_default(nthreads);
+    int bad = 0;
+    #pragma omp parallel for num_threads(nt) schedule(dynamic) reduction(|:bad)
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        int b = (int)(bh / H), h = (int)(bh % H);
+        int nv = n_valid ? n_valid[b] : T;
+        if (nv < 0 || nv > T) { bad |= 1; continue; }
+        int64_t s = slot ? slot[b] : b;
+        double *S = S_pool + (s * H + h) * (int64_t)P2 * d;
+        double *Z = Z_pool + (s * H + h) * (int64_t)P2;
+        const double *Wh = W + (int64_t)h * d * F;
+        double *u = (double *)malloc(sizeof(double) * F);
+        double *p = (double *)malloc(sizeof(double) * P2);
+        for (int t = 0; t < nv; ++t) {
+            const double *kt = k + (bh * T + t) * (int64_t)d;
+            const double *vt = v + (bh * T + t) * (int64_t)d;
+            phi_row(d, F, kt, Wh, u, p);
+            for (int f = 0; f < P2; ++f) {
+                Z[f] += p[f];
+                for (int n = 0; n < d; ++n) S[(int64_t)f * d + n] += p[f] * vt[n];
+            }
+        }
+        free(u);
+        free(p);
+    }
+    return bad ? 2 : 0;
+}
+
+/* One denoising step of block-hybrid attention (section 3.1):
+ *   within-block branch  a_j = exp(q.k_j / sqrt(d)),
+ *                        sm_num = sum_j a_j v_j,  sm_den = sum_j a_j
+ *                        (every query sees all L block tokens, no mask);
+ *   linear readout       lin_num = phi(q)^T S,  lin_den = phi(q)^T Z;
+ *   gated merge          out = (w sm_num + lin_num) / (w sm_den + lin_den).
+ * Scores are used unshifted, exactly as written; |score| above
+ * ORC_MAX_ABS_SCORE is refused (return 3) instead of overflowing. */
+int orc_step(int B, int H, int L, int d, int F, const double *q,
+             const double *k, const double *v, const double *W,
+             const double *gate, const double *S_pool, const double *Z_pool,
+             const int32_t *slot, double *out, int nthreads) {
+    if (B < 0 || H <= 0 || L <= 0 || d <= 0 || F <= 0) return 1;
+    const int P2 = 2 * F;
+    const double scale = 1.0 / sqrt((double)d);
+    int nt = threads_or_default(nthreads);
+    int bad = 0;
+    #pragma omp parallel for num_threads(nt) schedule(dynamic) reduction(|:bad)
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        int b = (int)(bh / H), h = (int)(bh % H);
+        int64_t s = slot ? slot[b] : b;
+        const double *S = S_pool + (s * H + h) * (int64_t)P2 * d;
+        const double *Z = Z_pool + (s * H + h) * (int64_t)P2;
+        const double *Wh = W + (int64_t)h * d * F;
+        const double w = gate ? gate[h] : 1.0;
+        const double *qb = q + bh * (int64_t)L * d;
+        const double *kb = k + bh * (int64_t)L * d;
+        const double *vb = v + bh * (int64_t)L * d;
+        double *ob = out + bh * (int64_t)L * d;
+        double *u = (double *)malloc(sizeof(double) * F);
+        double *p = (double *)malloc(sizeof(double) * P2);
+        double *num = (double *)malloc(sizeof(double) * d);
+        for (int i = 0; i < L; ++i) {
+            const double *qi = qb + (int64_t)i * d;
+            /* within-block softmax branch */
+            double sm_den = 0.0;
+            for (int n = 0; n < d; ++n) num[n] = 0.0;
+            for (int j = 0; j < L; ++j) {
+                double sc = 0.0;
+                for (int n = 0; n < d; ++n) sc += qi[n] * kb[(int64_t)j * d + n];
+                sc *= scale;
+                if (!(fabs(sc) <= ORC_MAX_ABS_SCORE)) bad |= 4;
+                double a = exp(sc);
+                sm_den += a;
+                for (int n = 0; n < d; ++n) num[n] += w * a * vb[(int64_t)j * d + n];
+            }
+            /* linear readout of the committed context */
+            phi_row(d, F, qi, Wh, u, p);
+            double lin_den = 0.0;
+            for (int f = 0; f < P2; ++f) lin_den += p[f] * Z[f];
+            for (int n = 0; n < d; ++n) {
+                double lin = 0.0;
+                for (int f = 0; f < P2; ++f) lin += p[f] * S[(int64_t)f * d + n];
+                num[n] += lin;
+            }
+            /* shared normaliser */
+            double den = w * sm_den + lin_den;
+            for (int n = 0; n < d; ++n) ob[(int64_t)i * d + n] = num[n] / den;
+        }
+        free(u);
+        free(p);
+        free(num);
+    }
+    return bad ? 3 : 0;
+}
+
+/* Full softmax attention of the active block's queries over the prefix cache
+ * and the block itself (section 2.2, softmax attention, with every prefix and
+ * block key visible to the block's queries): the comparator the hybrid
+ * layer replaces.  Request b uses the first prefix_len[b] cached tokens
+ * (max_prefix when NULL). */
+int orc_prefix_softmax(int B, int H, int L, int d, int max_prefix,
+                       const int32_t *prefix_len, const double *q,
+                       const double *k, const double *v, const double *Kc,
+                       const double *Vc, double *out, int nthreads) {
+    if (B < 0 || H <= 0 || L <= 0 || d <= 0 || max_prefix < 0) return 1;
+    const double scale = 1.0 / sqrt((double)d);
+    int nt = threads_or_default(nthreads);
+    int bad = 0;
+    #pragma omp parallel for num_threads(nt) schedule(dynamic) reduction(|:bad)
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        int b = (int)(bh / H);
+        int P = prefix_len ? prefix_len[b] : max_prefix;
+        if (P < 0 || P > max_prefix) { bad |= 2; continue; }
+        const double *qb = q + bh * (int64_t)L * d;
+        const double *kb = k + bh * (int64_t)L * d;
+        const double *vb = v + bh * (int64_t)L * d;
+        const double *Kb = Kc + bh * (int64_t)max_prefix * d;
+        const double *Vb = Vc + bh * (int64_t)max_prefix * d;
+        double *ob = out + bh * (int64_t)L * d;
+        double *num = (double *)malloc(sizeof(double) * d);
+        for (int i = 0; i < L; ++i) {
+            const double *qi = qb + (int64_t)i * d;
+            double den = 0.0;
+            for (int n = 0; n < d; ++n) num[n] = 0.0;
+            for (int j = 0; j < P + L; ++j) {
+                const double *kj = j < P ? Kb + (int64_t)j * d : kb + (int64_t)(j - P) * d;
+                const double *vj = j < P ? Vb + (int64_t)j * d : vb + (int64_t)(j - P) * d;
+                double sc = 0.0;
+                for (int n = 0; n < d; ++n) sc += qi[n] * kj[n];
+                sc *= scale;
+                if (!(fabs(sc) <= ORC_MAX_ABS_SCORE)) bad |= 4;
+                double a = exp(sc);
+                den += a;
+                for (int n = 0; n < d; ++n) num[n] += a * vj[n];
+            }
+            for (int n = 0; n < d; ++n) ob[(int64_t)i * d + n] = num[n] / den;
+        }
+        free(num);
+    }
+    return bad ? 3 : 0;
+}
