@@ -1,0 +1,118 @@
+// hba_api.cpp -- the C ABI declared in include/hba.h: host-side validation
+// and dispatch to the gfx950 kernels.  Nothing here allocates device memory
+// or synchronises; every call enqueues at most one kernel on the caller's
+// stream.
+#include "../../include/hba.h"
+
+#include <hip/hip_runtime.h>
+
+#include "hba_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+hba_status check_common(const hba_shape *s, bool need_block, bool need_feat) {
+    if (!s) return HBA_ERR_NULL;
+    if (s->in_dtype != HBA_F32 && s->in_dtype != HBA_BF16) return HBA_ERR_DTYPE;
+    if (s->batch < 0 || s->heads <= 0) return HBA_ERR_SHAPE;
+    if (s->head_dim != 64 && s->head_dim != 128) return HBA_ERR_UNSUPPORTED;
+    if (need_feat && s->feat != 64 && s->feat != 128) return HBA_ERR_UNSUPPORTED;
+    if (need_block && (s->block < 1 || s->block > 32)) {
+        return s->block < 1 ? HBA_ERR_SHAPE : HBA_ERR_UNSUPPORTED;
+    }
+    if ((int64_t)s->batch * s->heads > kMaxGrid) return HBA_ERR_SHAPE;
+    return HBA_OK;
+}
+
+hba_status from_hip(hipError_t e) { return e == hipSuccess ? HBA_OK : HBA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *hba_status_string(hba_status st) {
+    switch (st) {
+        case HBA_OK: return "ok";
+        case HBA_ERR_NULL: return "a required pointer is NULL";
+        case HBA_ERR_SHAPE: return "a size is out of range";
+        case HBA_ERR_UNSUPPORTED: return "unsupported (head_dim, feat, block) combination";
+        case HBA_ERR_DTYPE: return "in_dtype is not HBA_F32 or HBA_BF16";
+        case HBA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case HBA_ERR_CAPACITY: return "batch exceeds n_slots with no slot map";
+        case HBA_ERR_HIP: return "the HIP runtime refused the launch";
+    }
+    return "unknown status";
+}
+
+int32_t hba_abi_version(void) { return 1; }
+
+hba_status hba_feature_map(const hba_shape *shape, int64_t n_rows, const void *x, const void *W,
+                           float *phi, void *stream) {
+    hba_status st = check_common(shape, false, true);
+    if (st != HBA_OK) return st;
+    if (n_rows < 0 || n_rows >= ((int64_t)1 << 31)) return HBA_ERR_SHAPE;
+    if ((n_rows + 31) / 32 > kMaxGrid || shape->heads > 65535) return HBA_ERR_SHAPE;
+    if (n_rows == 0) return HBA_OK;
+    if (!x || !W || !phi) return HBA_ERR_NULL;
+    if (!aligned16(x) || !aligned16(W) || !aligned16(phi)) return HBA_ERR_ALIGN;
+    hba::FeatureMapArgs a{x, W, phi, n_rows, shape->heads};
+    return from_hip(hba::launch_feature_map(a, shape->in_dtype == HBA_BF16, shape->head_dim,
+                                            shape->feat, static_cast<hipStream_t>(stream)));
+}
+
+hba_status hba_step(const hba_shape *shape, const void *q, const void *k, const void *v,
+                    const void *W, const float *gate, const float *S_pool, const float *Z_pool,
+                    const int32_t *slot, float *out, void *stream) {
+    hba_status st = check_common(shape, true, true);
+    if (st != HBA_OK) return st;
+    if (shape->n_slots < 0) return HBA_ERR_SHAPE;
+    if (shape->batch == 0) return HBA_OK;
+    if (!q || !k || !v || !W || !S_pool || !Z_pool || !out) return HBA_ERR_NULL;
+    if (!slot && shape->batch > shape->n_slots) return HBA_ERR_CAPACITY;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(W) || !aligned16(S_pool) ||
+        !aligned16(Z_pool) || !aligned16(out) || (gate && !aligned4(gate)) || (slot && !aligned4(slot)))
+        return HBA_ERR_ALIGN;
+    hba::StepArgs a{q, k, v, W, gate, S_pool, Z_pool, slot, out, shape->batch, shape->heads, shape->block};
+    return from_hip(hba::launch_step(a, shape->in_dtype == HBA_BF16, shape->head_dim, shape->feat,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+hba_status hba_commit(const hba_shape *shape, int32_t n_tok, const int32_t *n_valid, const void *k,
+                      const void *v, const void *W, float *S_pool, float *Z_pool, const int32_t *slot,
+                      void *stream) {
+    hba_status st = check_common(shape, false, true);
+    if (st != HBA_OK) return st;
+    if (n_tok < 0 || shape->n_slots < 0) return HBA_ERR_SHAPE;
+    if (shape->batch == 0 || n_tok == 0) return HBA_OK;
+    if (!k || !v || !W || !S_pool || !Z_pool) return HBA_ERR_NULL;
+    if (!slot && shape->batch > shape->n_slots) return HBA_ERR_CAPACITY;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(W) || !aligned16(S_pool) || !aligned16(Z_pool) ||
+        (n_valid && !aligned4(n_valid)) || (slot && !aligned4(slot)))
+        return HBA_ERR_ALIGN;
+    hba::CommitArgs a{n_valid, k, v, W, S_pool, Z_pool, slot, shape->batch, shape->heads, n_tok};
+    return from_hip(hba::launch_commit(a, shape->in_dtype == HBA_BF16, shape->head_dim, shape->feat,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+hba_status hba_prefix_softmax(const hba_shape *shape, int32_t max_prefix, const int32_t *prefix_len,
+                              const void *q, const void *k, const void *v, const void *Kc,
+                              const void *Vc, float *out, void *stream) {
+    hba_status st = check_common(shape, true, false);
+    if (st != HBA_OK) return st;
+    if (max_prefix < 0 || (int64_t)max_prefix + shape->block > 0x7fffffff) return HBA_ERR_SHAPE;
+    if (shape->batch == 0) return HBA_OK;
+    if (!q || !k || !v || !out) return HBA_ERR_NULL;
+    if (max_prefix > 0 && (!Kc || !Vc)) return HBA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (max_prefix > 0 && (!aligned16(Kc) || !aligned16(Vc))) || (prefix_len && !aligned4(prefix_len)))
+        return HBA_ERR_ALIGN;
+    hba::PrefixArgs a{prefix_len, q, k, v, Kc, Vc, out, shape->batch, shape->heads, shape->block, max_prefix};
+    return from_hip(hba::launch_prefix_softmax(a, shape->in_dtype == HBA_BF16, shape->head_dim,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

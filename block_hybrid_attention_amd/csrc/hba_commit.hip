@@ -1,0 +1,205 @@
+// hba_commit.hip -- fold committed tokens into the recurrent states.
+//
+// "Retrofitting Linear Attention into Diffusion Language Models", section 3.1
+// (state update once a block is committed):
+//   S <- S + sum_t phi(k_t) v_t^T,   Z <- Z + sum_t phi(k_t).
+//
+// One workgroup (4 waves) per (request, head).  The commit is a read-modify-
+// write of the fp32 state (2 x 128 KB at F = d = 128) plus a small
+// contraction Phi^T V (K = tokens).  Design:
+//   * The old state is loaded straight into the MFMA accumulators at entry
+//     (wave w owns state rows [w 2F/4, (w+1) 2F/4)), so the contraction
+//     accumulates onto it and the result is stored once: one read and one
+//     write of S, both 512-byte-row coalesced.  To get that, the output column
+//     held by MFMA column j of N-tile e is d/16 * j + e, so each lane owns
+//     d/16 consecutive columns.
+//   * Tokens are processed in chunks of 32: k goes through LDS, u = k W runs
+//     on MFMA, phi(k) is formed per token row in fp32 and written over u in
+//     place (same row stride), then Phi^T V runs on fp32 MFMA.
+//   * Z is accumulated per feature by one thread each.
+//   * No atomics: each (request, head) state has exactly one writer, so the
+//     update is deterministic.
+#include "hba_device.h"
+#include "hba_internal.h"
+
+namespace hba {
+
+template <typename T, int D, int F>
+struct CommitGeom {
+    using P = ProjGeom<T, D, F>;
+    static constexpr int PLD = 2 * F + 16;   // phi row stride (floats); u shares it
+    static constexpr int k_off = 0;
+    static constexpr int w_off = P::x_bytes;
+    static constexpr int u_off = w_off + P::w_bytes;
+    static constexpr int bytes = u_off + kRows * PLD * 4;
+};
+
+// Load NE consecutive input elements (NE = d/16) and widen to fp32.
+template <typename T, int NE>
+__device__ __forceinline__ void load_cols(const T *__restrict__ p, float (&o)[NE]) {
+    constexpr int BYTES = NE * (int)sizeof(T);
+    if constexpr (BYTES == 32) {
+        const uint4 a = reinterpret_cast<const uint4 *>(p)[0];
+        const uint4 b = reinterpret_cast<const uint4 *>(p)[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = __uint_as_float(w[e]);
+    } else if constexpr (BYTES == 16) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(p);
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+        if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = __uint_as_float(w[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = bf16_bits_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        }
+    } else {  // 4 bf16 = 8 bytes
+        const uint2 a = *reinterpret_cast<const uint2 *>(p);
+        const uint32_t w[2] = {a.x, a.y};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = bf16_bits_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+    }
+}
+
+template <typename T, int D, int F>
+__global__ __launch_bounds__(kThreads) void commit_kernel(CommitArgs a) {
+    using G = CommitGeom<T, D, F>;
+    constexpr int NE = D / 16;        // N-tiles; a lane owns NE consecutive columns
+    constexpr int FW = 2 * F / 4;     // state rows owned by one wave
+    constexpr int MT = FW / 16;       // 16-row M-tiles per wave
+    constexpr int FM = F / 64;
+
+    __shared__ __attribute__((aligned(16))) char smem[G::bytes];
+    T *ks = reinterpret_cast<T *>(smem + G::k_off);
+    T *ws = reinterpret_cast<T *>(smem + G::w_off);
+    float *us = reinterpret_cast<float *>(smem + G::u_off);   // u, then phi, per row
+
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int bh = (int)blockIdx.x;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int T_ = a.T;
+    int nv = a.n_valid ? a.n_valid[b] : T_;
+    nv = nv < 0 ? 0 : (nv > T_ ? T_ : nv);
+    const int64_t slot = a.slot ? (int64_t)a.slot[b] : (int64_t)b;
+
+    const T *kg = static_cast<const T *>(a.k) + (int64_t)bh * T_ * D;
+    const T *vg = static_cast<const T *>(a.v) + (int64_t)bh * T_ * D;
+    const T *Wg = static_cast<const T *>(a.W) + (int64_t)h * D * F;
+    float *Sg = a.S + (slot * a.H + h) * (int64_t)(2 * F) * D;
+    float *Zg = a.Z + (slot * a.H + h) * (int64_t)(2 * F);
+    if (nv == 0) return;   // nothing to fold; the state is left untouched
+
+    WChunks<T, D, F> wc;
+    load_w<T, D, F>(Wg, wc);
+
+    // old state straight into the accumulators
+    const int f_base = wave * FW;
+    floatx4 acc[MT][NE];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float *p = Sg + (int64_t)(f_base + 16 * mt + 4 * lg + r) * D + NE * li;
+#pragma unroll
+            for (int q = 0; q < NE / 4; ++q) {
+                const float4 t = reinterpret_cast<const float4 *>(p)[q];
+                acc[mt][4 * q + 0][r] = t.x;
+                acc[mt][4 * q + 1][r] = t.y;
+                acc[mt][4 * q + 2][r] = t.z;
+                acc[mt][4 * q + 3][r] = t.w;
+            }
+        }
+    }
+    float zacc = tid < 2 * F ? Zg[tid] : 0.f;
+    store_w<T, D, F>(wc, ws);
+
+#pragma unroll 1
+    for (int t0 = 0; t0 < nv; t0 += kRows) {
+        const int nrows = nv - t0 < kRows ? nv - t0 : kRows;
+        // B operand: v rows t0 + 4 kk + lg, columns NE*li .. NE*li + NE - 1
+        float vop[8][NE];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const int j = 4 * kk + lg;
+            load_cols<T, NE>(vg + (int64_t)(t0 + (j < nrows ? j : nrows - 1)) * D + NE * li, vop[kk]);
+#pragma unroll
+            for (int e = 0; e < NE; ++e) vop[kk][e] = j < nrows ? vop[kk][e] : 0.f;
+        }
+        stage_rows<T, D, F>(kg + (int64_t)t0 * D, D, nrows, ks);
+        __syncthreads();
+        project_tile<T, D, F, G::PLD>(ks, ws, us);
+        __syncthreads();
+        // phi(k_t) per token row, written over u in place; rows past the end are 0
+#pragma unroll 1
+        for (int ii = 0; ii < 8; ++ii) {
+            const int i = 8 * wave + ii;
+            float *row = us + i * G::PLD;
+            if (i < nrows) {
+                float pp[FM], pn[FM];
+                phi_of_row<F>(row, lane, pp, pn);
+#pragma unroll
+                for (int m = 0; m < FM; ++m) {
+                    row[lane + 64 * m] = pp[m];
+                    row[F + lane + 64 * m] = pn[m];
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < 2 * FM; ++m) row[lane + 64 * m] = 0.f;
+            }
+        }
+        __syncthreads();
+        if (tid < 2 * F) {
+            float zs = 0.f;
+#pragma unroll 8
+            for (int i = 0; i < kRows; ++i) zs += us[i * G::PLD + tid];
+            zacc += zs;
+        }
+        // S += Phi^T V : A[f][t] = phi_f(k_t), B[t][col] = v_t[col]
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const float av = us[(4 * kk + lg) * G::PLD + f_base + 16 * mt + li];
+#pragma unroll
+                for (int e = 0; e < NE; ++e) acc[mt][e] = mfma_f32(av, vop[kk][e], acc[mt][e]);
+            }
+        }
+        __syncthreads();   // the next chunk reuses the k tile and u/phi rows
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float *p = Sg + (int64_t)(f_base + 16 * mt + 4 * lg + r) * D + NE * li;
+#pragma unroll
+            for (int q = 0; q < NE / 4; ++q)
+                reinterpret_cast<float4 *>(p)[q] = make_float4(acc[mt][4 * q + 0][r], acc[mt][4 * q + 1][r],
+                                                                acc[mt][4 * q + 2][r], acc[mt][4 * q + 3][r]);
+        }
+    }
+    if (tid < 2 * F) Zg[tid] = zacc;
+}
+
+template <typename T, int D, int F>
+static hipError_t launch_commit_t(const CommitArgs &a, hipStream_t stream) {
+    return launch_kernel(commit_kernel<T, D, F>, dim3((unsigned)(a.B * a.H)), dim3(kThreads), a, stream);
+}
+
+hipError_t launch_commit(const CommitArgs &a, bool bf16, int d, int F, hipStream_t stream) {
+#define HBA_COMMIT_CASE(DD, FF)                                                            \
+    if (d == DD && F == FF)                                                                \
+        return bf16 ? launch_commit_t<uint16_t, DD, FF>(a, stream)                         \
+                    : launch_commit_t<float, DD, FF>(a, stream);
+    HBA_COMMIT_CASE(64, 64)
+    HBA_COMMIT_CASE(64, 128)
+    HBA_COMMIT_CASE(128, 64)
+    HBA_COMMIT_CASE(128, 128)
+#undef HBA_COMMIT_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace hba

@@ -1,0 +1,255 @@
+// hba_device.h -- device-side building blocks shared by the block-hybrid
+// attention kernels (gfx950 / CDNA4, wave64).
+//
+// Tiles are 32 rows (tokens) by d columns.  Matrix products use the gfx950
+// MFMA instructions:
+//   v_mfma_f32_16x16x32_bf16  for bf16 x bf16 products (exact in fp32),
+//   v_mfma_f32_16x16x4_f32    for fp32 operands.
+// Lane layouts (wave64, lane l):
+//   16x16x32 bf16: A[i = l%16][k = 8(l/16) .. 8(l/16)+7], B[k = same][j = l%16]
+//   16x16x4  f32 : A[i = l%16][k = l/16],                 B[k = l/16][j = l%16]
+//   accumulator  : D[i = 4(l/16) + r][j = l%16], r = 0..3 (vector element r)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hba {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;   // 4 waves per workgroup
+constexpr int kRows = 32;       // rows of a token tile (the block size bound)
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+    return __uint_as_float(h << 16);
+}
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return bf16_bits_to_f32(x); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ floatx4 mfma_f32(float a, float b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma_bf16(bf16x8 a, bf16x8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// exp(x) through the hardware base-2 exponential.
+__device__ __forceinline__ float fast_exp(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// ---------------------------------------------------------------------------
+// LDS geometry of the projection stage, per input element type.
+//   X tile : [32][XLD] rows of x (q, k or x), bf16 or fp32
+//   W      : bf16 -> transposed Wt[F][XLD] (row f holds column f of W),
+//            fp32 -> as given, W[D][F + 16]
+//   u      : [32][F + 4] fp32, u = X W
+// Row paddings keep the MFMA operand reads free of LDS bank conflicts.
+template <typename T, int D, int F>
+struct ProjGeom {
+    static constexpr bool kBf16 = sizeof(T) == 2;
+    static constexpr int XLD = kBf16 ? D + 8 : D + 4;            // elements
+    static constexpr int WROWS = kBf16 ? F : D;
+    static constexpr int WLD = kBf16 ? D + 8 : F + 16;           // elements
+    static constexpr int ULD = F + 4;                            // floats
+    static constexpr int x_bytes = kRows * XLD * (int)sizeof(T);
+    static constexpr int w_bytes = WROWS * WLD * (int)sizeof(T);
+    static constexpr int u_bytes = kRows * ULD * 4;
+};
+
+// Copy `nrows` (1..32) rows of D elements, global row stride `gstride`
+// elements, into an LDS tile [32][XLD]; rows >= nrows are zero-filled.
+// Branch-free, so loads already in flight are not forced to drain.
+template <typename T, int D, int F>
+__device__ __forceinline__ void stage_rows(const T *__restrict__ g, int64_t gstride, int nrows,
+                                           T *__restrict__ xs) {
+    using G = ProjGeom<T, D, F>;
+    constexpr int EPC = 16 / (int)sizeof(T);        // elements per 16-byte chunk
+    constexpr int CPR = D / EPC;                    // chunks per row
+    constexpr int N = kRows * CPR;
+    static_assert(N % kThreads == 0, "tile chunks must divide the workgroup");
+#pragma unroll
+    for (int it = 0; it < N / kThreads; ++it) {
+        const int c = (int)threadIdx.x + it * kThreads;
+        const int r = c / CPR, col = (c % CPR) * EPC;
+        const int rr = r < nrows ? r : nrows - 1;
+        const uint4 t = *reinterpret_cast<const uint4 *>(g + (int64_t)rr * gstride + col);
+        const bool ok = r < nrows;
+        *reinterpret_cast<uint4 *>(xs + r * G::XLD + col) =
+            make_uint4(ok ? t.x : 0u, ok ? t.y : 0u, ok ? t.z : 0u, ok ? t.w : 0u);
+    }
+}
+
+// Two-phase variant used where the global loads should be issued early and
+// the LDS writes done later: load into registers, then store.  Requires
+// nrows >= 1.
+template <typename T, int D>
+struct RowChunks {
+    static constexpr int EPC = 16 / (int)sizeof(T);
+    static constexpr int CPR = D / EPC;
+    static constexpr int N = kRows * CPR / kThreads;
+    uint4 v[N];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void load_rows(const T *__restrict__ g, int64_t gstride, int nrows,
+                                          RowChunks<T, D> &rc) {
+    constexpr int EPC = RowChunks<T, D>::EPC, CPR = RowChunks<T, D>::CPR;
+#pragma unroll
+    for (int it = 0; it < RowChunks<T, D>::N; ++it) {
+        const int c = (int)threadIdx.x + it * kThreads;
+        const int r = c / CPR, col = (c % CPR) * EPC;
+        // branch-free: read a valid row (nrows >= 1), then zero rows past the
+        // end, so no control flow forces the in-flight loads to drain
+        const int rr = r < nrows ? r : nrows - 1;
+        uint4 t = *reinterpret_cast<const uint4 *>(g + (int64_t)rr * gstride + col);
+        const bool ok = r < nrows;
+        rc.v[it] = make_uint4(ok ? t.x : 0u, ok ? t.y : 0u, ok ? t.z : 0u, ok ? t.w : 0u);
+    }
+}
+
+template <typename T, int D, int F>
+__device__ __forceinline__ void store_rows(const RowChunks<T, D> &rc, T *__restrict__ xs) {
+    using G = ProjGeom<T, D, F>;
+    constexpr int EPC = RowChunks<T, D>::EPC, CPR = RowChunks<T, D>::CPR;
+#pragma unroll
+    for (int it = 0; it < RowChunks<T, D>::N; ++it) {
+        const int c = (int)threadIdx.x + it * kThreads;
+        const int r = c / CPR, col = (c % CPR) * EPC;
+        *reinterpret_cast<uint4 *>(xs + r * G::XLD + col) = rc.v[it];
+    }
+}
+
+// W [D][F] of one head (global) -> LDS in the layout ProjGeom describes.
+template <typename T, int D, int F>
+struct WChunks {
+    static constexpr int EPC = 16 / (int)sizeof(T);
+    static constexpr int N = D * F / EPC / kThreads;
+    uint4 v[N];
+};
+
+template <typename T, int D, int F>
+__device__ __forceinline__ void load_w(const T *__restrict__ W, WChunks<T, D, F> &wc) {
+    constexpr int EPC = WChunks<T, D, F>::EPC;
+#pragma unroll
+    for (int it = 0; it < WChunks<T, D, F>::N; ++it) {
+        const int c = (int)threadIdx.x + it * kThreads;
+        wc.v[it] = *reinterpret_cast<const uint4 *>(W + (int64_t)c * EPC);
+    }
+}
+
+template <typename T, int D, int F>
+__device__ __forceinline__ void store_w(const WChunks<T, D, F> &wc, T *__restrict__ ws) {
+    using G = ProjGeom<T, D, F>;
+    constexpr int EPC = WChunks<T, D, F>::EPC;
+    constexpr int CPR = F / EPC;   // chunks per W row
+#pragma unroll
+    for (int it = 0; it < WChunks<T, D, F>::N; ++it) {
+        const int c = (int)threadIdx.x + it * kThreads;
+        const int i = c / CPR, f0 = (c % CPR) * EPC;
+        if constexpr (G::kBf16) {
+            // scatter the 8 features of row i into column i of Wt[f][.]
+            const uint32_t w4[4] = {wc.v[it].x, wc.v[it].y, wc.v[it].z, wc.v[it].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint16_t h = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+                ws[(f0 + e) * G::WLD + i] = h;
+            }
+        } else {
+            *reinterpret_cast<uint4 *>(ws + i * G::WLD + f0) = wc.v[it];
+        }
+    }
+}
+
+// u = X W for a 32-row tile: X tile and W staged in LDS; u written to LDS.
+// The 2 x (F/16) output tiles of 16x16 are spread over the 4 waves.
+template <typename T, int D, int F, int ULD = ProjGeom<T, D, F>::ULD>
+__device__ __forceinline__ void project_tile(const T *__restrict__ xs, const T *__restrict__ ws,
+                                             float *__restrict__ us) {
+    using G = ProjGeom<T, D, F>;
+    const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    constexpr int TILES = 2 * (F / 16);
+    static_assert(TILES % 4 == 0, "tiles must split evenly over 4 waves");
+#pragma unroll
+    for (int q = 0; q < TILES / 4; ++q) {
+        const int tau = wave + 4 * q;
+        const int mt = tau & 1, nt = tau >> 1;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (G::kBf16) {
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(xs + (16 * mt + li) * G::XLD + 32 * ks + 8 * lg);
+                const bf16x8 b = *reinterpret_cast<const bf16x8 *>(ws + (16 * nt + li) * G::WLD + 32 * ks + 8 * lg);
+                acc = mfma_bf16(a, b, acc);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < D / 4; ++ks) {
+                const float a = xs[(16 * mt + li) * G::XLD + 4 * ks + lg];
+                const float b = ws[(4 * ks + lg) * G::WLD + 16 * nt + li];
+                acc = mfma_f32(a, b, acc);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) us[(16 * mt + 4 * lg + r) * ULD + 16 * nt + li] = acc[r];
+    }
+}
+
+// Hedgehog feature map of one staged row, computed by one wave
+// ("Retrofitting Linear Attention into Diffusion Language Models", section 3.1):
+//   phi = [softmax(u), softmax(-u)],  u = x W.
+// Lane l ends with phi_pos[m] = phi[l + 64 m] and phi_neg[m] = phi[F + l + 64 m].
+template <int F>
+__device__ __forceinline__ void phi_of_row(const float *__restrict__ urow, int lane,
+                                           float (&phi_pos)[F / 64], float (&phi_neg)[F / 64]) {
+    static_assert(F % 64 == 0, "F must be a multiple of 64");
+    float u[F / 64];
+    float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+    for (int m = 0; m < F / 64; ++m) {
+        u[m] = urow[lane + 64 * m];
+        mx = fmaxf(mx, u[m]);
+        mn = fminf(mn, u[m]);
+    }
+    mx = wave_max(mx);
+    mn = wave_min(mn);
+    float sp = 0.f, sn = 0.f;
+#pragma unroll
+    for (int m = 0; m < F / 64; ++m) {
+        phi_pos[m] = fast_exp(u[m] - mx);   // <= 1
+        phi_neg[m] = fast_exp(mn - u[m]);   // <= 1
+        sp += phi_pos[m];
+        sn += phi_neg[m];
+    }
+    sp = wave_sum(sp);
+    sn = wave_sum(sn);
+    const float ip = 1.0f / sp, in = 1.0f / sn;
+#pragma unroll
+    for (int m = 0; m < F / 64; ++m) {
+        phi_pos[m] *= ip;
+        phi_neg[m] *= in;
+    }
+}
+
+}  // namespace hba

@@ -1,0 +1,65 @@
+// hba_internal.h -- kernel argument blocks and launchers behind the C ABI.
+// Host validation (hba_api.cpp) has already checked every size, pointer and
+// alignment the kernels rely on when these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hba {
+
+struct FeatureMapArgs {
+    const void *x;       // [n][H][d]
+    const void *W;       // [H][d][F]
+    float *phi;          // [n][H][2F]
+    int64_t n;
+    int H;
+};
+
+struct StepArgs {
+    const void *q, *k, *v;   // [B][H][L][d]
+    const void *W;           // [H][d][F]
+    const float *gate;       // [H] or null
+    const float *S;          // [slots][H][2F][d]
+    const float *Z;          // [slots][H][2F]
+    const int32_t *slot;     // [B] or null
+    float *out;              // [B][H][L][d]
+    int B, H, L;
+};
+
+struct CommitArgs {
+    const int32_t *n_valid;  // [B] or null
+    const void *k, *v;       // [B][H][T][d]
+    const void *W;           // [H][d][F]
+    float *S;                // [slots][H][2F][d]
+    float *Z;                // [slots][H][2F]
+    const int32_t *slot;     // [B] or null
+    int B, H, T;
+};
+
+struct PrefixArgs {
+    const int32_t *prefix_len;  // [B] or null
+    const void *q, *k, *v;      // [B][H][L][d]
+    const void *Kc, *Vc;        // [B][H][P][d]
+    float *out;                 // [B][H][L][d]
+    int B, H, L, P;
+};
+
+// Enqueue kernel `k` with a single by-value argument block on `stream`; the
+// returned status is this launch's own.
+template <typename Args>
+inline hipError_t launch_kernel(void (*k)(Args), dim3 grid, dim3 block, const Args &a,
+                                hipStream_t stream) {
+    void *args[] = {const_cast<Args *>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void *>(k), grid, block, args, 0, stream);
+}
+
+// Each launcher enqueues one kernel on `stream`; dtype_bf16 selects the
+// element type of the inputs.  Returns the launch status.
+hipError_t launch_feature_map(const FeatureMapArgs &a, bool dtype_bf16, int d, int F,
+                              hipStream_t stream);
+hipError_t launch_step(const StepArgs &a, bool dtype_bf16, int d, int F, hipStream_t stream);
+hipError_t launch_commit(const CommitArgs &a, bool dtype_bf16, int d, int F, hipStream_t stream);
+hipError_t launch_prefix_softmax(const PrefixArgs &a, bool dtype_bf16, int d, hipStream_t stream);
+
+}  // namespace hba

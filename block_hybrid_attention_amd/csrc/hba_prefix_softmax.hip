@@ -1,0 +1,258 @@
+// hba_prefix_softmax.hip -- full softmax attention over [prefix cache ; block].
+//
+// The comparator for block-hybrid attention: the exact softmax attention of
+// "Retrofitting Linear Attention into Diffusion Language Models", section 2.2,
+// for the active block's queries over every cached prefix token and every
+// block token (all visible, scale 1/sqrt d, no gate).  Its cost grows with the
+// prefix P, which is what the hybrid step's fixed-size state avoids.
+//
+// One workgroup (4 waves) per (request, head); the waves take interleaved
+// 16-key tiles and keep their own online-softmax state, merged in LDS at the
+// end.  Per tile:
+//   S^T = K Q^T on bf16 MFMA (fp32 MFMA for fp32 inputs): the accumulator
+//   layout gives each lane the scores of ONE query for four keys;
+//   O^T += V^T P^T on fp32 MFMA, whose B operand is exactly those four
+//   probabilities, so P never leaves registers and the per-query running max
+//   and sum live in the same lanes as the output rows they rescale.
+// The next tile's K and V are loaded before the current one is computed.
+#include "hba_device.h"
+#include "hba_internal.h"
+
+namespace hba {
+
+template <typename T, int D>
+struct PrefixOps {
+    static constexpr bool kBf16 = sizeof(T) == 2;
+    static constexpr int NCT = D / 16;                      // output column tiles
+    static constexpr int KREG = kBf16 ? D / 32 : D / 4;     // K operand registers per lane
+    static constexpr int VBYTES = NCT * (int)sizeof(T);     // per V row per lane
+    static constexpr int VQ = VBYTES / 16 > 0 ? VBYTES / 16 : 1;
+    // K operand: bf16 -> D/32 chunks of 8 bf16; fp32 -> D/4 floats
+    uint4 kq[kBf16 ? D / 32 : 1];
+    float kf[kBf16 ? 1 : D / 4];
+    uint4 vq[4][VBYTES >= 16 ? VBYTES / 16 : 1];
+    uint2 vh[4];   // used only when a V row slice is 8 bytes (bf16, d = 64)
+};
+
+template <typename T, int D>
+__device__ __forceinline__ const T *key_row(const PrefixArgs &a, int64_t bh, int P, int j) {
+    // virtual concatenation [prefix cache ; block]; caller clamps j < P + L
+    return j < P ? static_cast<const T *>(a.Kc) + (bh * a.P + j) * D
+                 : static_cast<const T *>(a.k) + (bh * a.L + (j - P)) * D;
+}
+template <typename T, int D>
+__device__ __forceinline__ const T *val_row(const PrefixArgs &a, int64_t bh, int P, int j) {
+    return j < P ? static_cast<const T *>(a.Vc) + (bh * a.P + j) * D
+                 : static_cast<const T *>(a.v) + (bh * a.L + (j - P)) * D;
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_tile(const PrefixArgs &a, int64_t bh, int P, int nkeys, int j0,
+                                          int li, int lg, PrefixOps<T, D> &op) {
+    using O = PrefixOps<T, D>;
+    // K row for this lane: key j0 + li (clamped; masked later)
+    int jk = j0 + li;
+    jk = jk < nkeys ? jk : nkeys - 1;
+    const T *kr = key_row<T, D>(a, bh, P, jk);
+    if constexpr (O::kBf16) {
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) op.kq[s] = *reinterpret_cast<const uint4 *>(kr + 32 * s + 8 * lg);
+    } else {
+#pragma unroll
+        for (int s = 0; s < D / 4; ++s) op.kf[s] = kr[4 * s + lg];
+    }
+    // V rows for this lane: keys j0 + 4 lg + r, columns NCT*li .. NCT*li + NCT - 1
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        int jv = j0 + 4 * lg + r;
+        jv = jv < nkeys ? jv : nkeys - 1;
+        const T *vr = val_row<T, D>(a, bh, P, jv) + O::NCT * li;
+        if constexpr (O::VBYTES >= 16) {
+#pragma unroll
+            for (int q = 0; q < O::VBYTES / 16; ++q) op.vq[r][q] = reinterpret_cast<const uint4 *>(vr)[q];
+        } else {
+            op.vh[r] = *reinterpret_cast<const uint2 *>(vr);
+        }
+    }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void v_row_f32(const PrefixOps<T, D> &op, int r, float (&o)[D / 16]) {
+    using O = PrefixOps<T, D>;
+    if constexpr (O::VBYTES >= 16) {
+#pragma unroll
+        for (int q = 0; q < O::VBYTES / 16; ++q) {
+            const uint32_t w[4] = {op.vq[r][q].x, op.vq[r][q].y, op.vq[r][q].z, op.vq[r][q].w};
+            if constexpr (O::kBf16) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[8 * q + e] = bf16_bits_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[4 * q + e] = __uint_as_float(w[e]);
+            }
+        }
+    } else {
+        const uint32_t w[2] = {op.vh[r].x, op.vh[r].y};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = bf16_bits_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+    }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void prefix_kernel(PrefixArgs a) {
+    using O = PrefixOps<T, D>;
+    constexpr int NCT = O::NCT;
+    constexpr int OLD = D + 4;   // merge buffer row stride (floats)
+    constexpr float kScaleLog2 = (D == 128 ? 0.08838834764831845f : 0.125f) * 1.4426950408889634f;
+    __shared__ __attribute__((aligned(16))) float obuf[4 * kRows * OLD];
+    __shared__ float mbuf[4][kRows], lbuf[4][kRows];
+
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int64_t bh = blockIdx.x;
+    const int b = (int)(bh / a.H);
+    const int L = a.L;
+    int P = a.prefix_len ? a.prefix_len[b] : a.P;
+    P = P < 0 ? 0 : (P > a.P ? a.P : P);
+    const int nkeys = P + L;
+    const int ntiles = (nkeys + 15) / 16;
+
+    // queries as the B operand of S^T = K Q^T: lane holds query 16 nt + li
+    const T *qg = static_cast<const T *>(a.q) + bh * L * D;
+    uint4 qq[2][O::kBf16 ? D / 32 : 1];
+    float qf[2][O::kBf16 ? 1 : D / 4];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int qi = 16 * nt + li;
+        const T *qr = qg + (int64_t)(qi < L ? qi : L - 1) * D;
+        if constexpr (O::kBf16) {
+#pragma unroll
+            for (int s = 0; s < D / 32; ++s) {
+                const uint4 t = *reinterpret_cast<const uint4 *>(qr + 32 * s + 8 * lg);
+                qq[nt][s] = qi < L ? t : make_uint4(0u, 0u, 0u, 0u);
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < D / 4; ++s) qf[nt][s] = qi < L ? qr[4 * s + lg] : 0.f;
+        }
+    }
+
+    floatx4 o[NCT][2];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) o[c][0] = o[c][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+
+    PrefixOps<T, D> cur, nxt;
+    if (wave < ntiles) load_tile<T, D>(a, bh, P, nkeys, 16 * wave, li, lg, cur);
+#pragma unroll 1
+    for (int tile = wave; tile < ntiles; tile += 4) {
+        const int j0 = 16 * tile;
+        {   // prefetch the wave's next tile (clamped to the last one)
+            const int tn = tile + 4 < ntiles ? tile + 4 : ntiles - 1;
+            load_tile<T, D>(a, bh, P, nkeys, 16 * tn, li, lg, nxt);
+        }
+        floatx4 s[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            s[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (O::kBf16) {
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks)
+                    s[nt] = mfma_bf16(*reinterpret_cast<const bf16x8 *>(&cur.kq[ks]),
+                                      *reinterpret_cast<const bf16x8 *>(&qq[nt][ks]), s[nt]);
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < D / 4; ++ks) s[nt] = mfma_f32(cur.kf[ks], qf[nt][ks], s[nt]);
+            }
+        }
+        float p[2][4];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            float x[4];
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                x[r] = (j0 + 4 * lg + r) < nkeys ? s[nt][r] * kScaleLog2 : -INFINITY;
+                tmax = fmaxf(tmax, x[r]);
+            }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+            const float mnew = fmaxf(m[nt], tmax);   // finite: every tile has a valid key
+            const float corr = __builtin_amdgcn_exp2f(m[nt] - mnew);
+            float rs = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[nt][r] = __builtin_amdgcn_exp2f(x[r] - mnew);
+                rs += p[nt][r];
+            }
+            rs += __shfl_xor(rs, 16, kWave);
+            rs += __shfl_xor(rs, 32, kWave);
+            l[nt] = l[nt] * corr + rs;
+            m[nt] = mnew;
+#pragma unroll
+            for (int c = 0; c < NCT; ++c) o[c][nt] *= corr;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float vv[NCT];
+            v_row_f32<T, D>(cur, r, vv);
+#pragma unroll
+            for (int c = 0; c < NCT; ++c) {
+                o[c][0] = mfma_f32(vv[c], p[0][r], o[c][0]);
+                o[c][1] = mfma_f32(vv[c], p[1][r], o[c][1]);
+            }
+        }
+        cur = nxt;
+    }
+
+    // merge the four waves' partial softmax states
+    if (lg == 0) {
+        mbuf[wave][li] = m[0];
+        mbuf[wave][16 + li] = m[1];
+        lbuf[wave][li] = l[0];
+        lbuf[wave][16 + li] = l[1];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int qi = 16 * nt + li;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, mbuf[w][qi]);
+        float Lt = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) Lt += lbuf[w][qi] * __builtin_amdgcn_exp2f(mbuf[w][qi] - M);
+        const float sc = __builtin_amdgcn_exp2f(m[nt] - M) / Lt;
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                obuf[(wave * kRows + qi) * OLD + NCT * (4 * lg + r) + c] = o[c][nt][r] * sc;
+    }
+    __syncthreads();
+    float *og = a.out + bh * L * D;
+#pragma unroll
+    for (int it = 0; it < kRows * D / kThreads; ++it) {
+        const int e = tid + it * kThreads;
+        const int qi = e / D, c = e % D;
+        if (qi < L) {
+            const float v = obuf[(0 * kRows + qi) * OLD + c] + obuf[(1 * kRows + qi) * OLD + c] +
+                            obuf[(2 * kRows + qi) * OLD + c] + obuf[(3 * kRows + qi) * OLD + c];
+            og[(int64_t)qi * D + c] = v;
+        }
+    }
+}
+
+template <typename T, int D>
+static hipError_t launch_prefix_t(const PrefixArgs &a, hipStream_t stream) {
+    return launch_kernel(prefix_kernel<T, D>, dim3((unsigned)(a.B * a.H)), dim3(kThreads), a, stream);
+}
+
+hipError_t launch_prefix_softmax(const PrefixArgs &a, bool bf16, int d, hipStream_t stream) {
+    if (d == 64) return bf16 ? launch_prefix_t<uint16_t, 64>(a, stream) : launch_prefix_t<float, 64>(a, stream);
+    if (d == 128) return bf16 ? launch_prefix_t<uint16_t, 128>(a, stream) : launch_prefix_t<float, 128>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace hba

@@ -1,0 +1,158 @@
+/*
+ * hba.h -- C ABI of the block-hybrid attention library (libhba.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is block-hybrid attention from "Retrofitting Linear Attention
+ * into Diffusion Language Models" (arXiv 2608.06628), section 3.1: during
+ * blockwise semi-autoregressive diffusion decoding, each query of the active
+ * block attends with exact bidirectional softmax to the block's own tokens
+ * and reads all previously committed blocks through fixed-size per-head
+ * linear-attention states built with the Hedgehog feature map; both parts
+ * share one normaliser.  Committing a finished block folds its keys and
+ * values into the states.
+ *
+ * Conventions shared by every call
+ *   - Pure C.  Every buffer is caller-owned device memory (pointers from
+ *     hipMalloc or a framework allocator); the library allocates nothing and
+ *     keeps no global state, so calls are thread-safe.
+ *   - Calls enqueue kernels on `stream` (a hipStream_t passed as void*; NULL
+ *     is the default stream) and return without synchronising.  A fault on
+ *     the device surfaces at the caller's next synchronisation.
+ *   - Host-checkable problems return a status and launch nothing: NULL
+ *     pointers, non-positive or too-large sizes, unsupported (d, F, L, dtype),
+ *     pointers not aligned to 16 bytes.  A launch failure returns
+ *     HBA_ERR_HIP.
+ *   - Values that live on the device (slot indices, per-request lengths, gate
+ *     values) cannot be checked without a synchronisation, so their ranges are
+ *     preconditions stated per call; violating one is undefined behaviour.
+ *   - All arrays are dense and row-major (C order) with the shapes given.
+ *     Offsets are computed in 64 bits, so a state pool may exceed 2^31
+ *     elements.
+ *   - Supported shapes: head_dim d in {64, 128}; feat F in {64, 128} (the
+ *     feature map has 2F entries); block L in [1, 32]; heads H >= 1.
+ *   - in_dtype selects the element type of q, k, v, x, W, Kc and Vc:
+ *     HBA_F32 (float) or HBA_BF16 (bfloat16 stored as uint16).  States S, Z,
+ *     feature-map output and attention outputs are always fp32; every
+ *     accumulation is fp32.
+ */
+#ifndef HBA_H
+#define HBA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HBA_F32 = 0,
+    HBA_BF16 = 1
+} hba_dtype;
+
+typedef enum {
+    HBA_OK = 0,
+    HBA_ERR_NULL = 1,         /* a required pointer is NULL */
+    HBA_ERR_SHAPE = 2,        /* a size is negative, zero where not allowed, or too large */
+    HBA_ERR_UNSUPPORTED = 3,  /* (d, F, L) outside the supported set */
+    HBA_ERR_DTYPE = 4,        /* in_dtype is not an hba_dtype */
+    HBA_ERR_ALIGN = 5,        /* a pointer is not 16-byte aligned */
+    HBA_ERR_CAPACITY = 6,     /* batch > n_slots while slot == NULL */
+    HBA_ERR_HIP = 7           /* the HIP runtime refused a launch */
+} hba_status;
+
+/* Problem shape shared by the calls.  Fields a call does not use are
+ * ignored by it (each call lists the fields it reads). */
+typedef struct {
+    int32_t batch;     /* B: requests in this call */
+    int32_t heads;     /* H: query heads (one state and one W per head) */
+    int32_t block;     /* L: tokens in the active block, 1..32 */
+    int32_t head_dim;  /* d: 64 or 128 */
+    int32_t feat;      /* F: 64 or 128; phi(x) has 2F entries */
+    int32_t in_dtype;  /* hba_dtype of q, k, v, x, W, Kc, Vc */
+    int64_t n_slots;   /* slots in the S/Z pool (hba_step, hba_commit) */
+} hba_shape;
+
+/* Hedgehog feature map (section 3.1):
+ *   phi(x) = [softmax(x W), softmax(-x W)] in R^{2F}, W in R^{d x F} per head,
+ * each softmax taken over the F features.
+ * Reads: heads, head_dim, feat, in_dtype.
+ *   x    [n_rows][H][d]   in_dtype
+ *   W    [H][d][F]        in_dtype
+ *   phi  [n_rows][H][2F]  fp32 output; phi[..][0:F] = softmax(xW),
+ *                         phi[..][F:2F] = softmax(-xW)
+ * n_rows = 0 is a no-op; n_rows must be < 2^31. */
+hba_status hba_feature_map(const hba_shape *shape, int64_t n_rows, const void *x,
+                           const void *W, float *phi, void *stream);
+
+/* One denoising step of block-hybrid attention (section 3.1), for every
+ * request b < B, head h < H and query i < L of the active block:
+ *   a_j     = exp(q_i . k_j / sqrt(d))            for all j < L (no mask)
+ *   sm_num  = sum_j a_j v_j,  sm_den = sum_j a_j
+ *   lin_num = phi(q_i)^T S,   lin_den = phi(q_i)^T Z   (S, Z of the request)
+ *   out_i   = (w sm_num + lin_num) / (w sm_den + lin_den),  w = gate[h]
+ * The kernels apply one exponent shift per query to both branches, which
+ * leaves the ratio unchanged and keeps every term finite.
+ * Reads: batch, heads, block, head_dim, feat, in_dtype, n_slots.
+ *   q, k, v  [B][H][L][d]        in_dtype, the active block
+ *   W        [H][d][F]           in_dtype
+ *   gate     [H] fp32 or NULL    w = sigma(alpha) per head; NULL means w = 1.
+ *                                Precondition: 0 < w < inf.
+ *   S_pool   [n_slots][H][2F][d] fp32, S = sum_t phi(k_t) v_t^T (read only)
+ *   Z_pool   [n_slots][H][2F]    fp32, Z = sum_t phi(k_t)      (read only)
+ *   slot     [B] int32 or NULL   pool slot of request b; NULL means slot b
+ *                                (then B <= n_slots is checked).
+ *                                Precondition: 0 <= slot[b] < n_slots.
+ *   out      [B][H][L][d]        fp32 output
+ * An empty state (S = 0, Z = 0) gives exact softmax within the block. */
+hba_status hba_step(const hba_shape *shape, const void *q, const void *k, const void *v,
+                    const void *W, const float *gate, const float *S_pool,
+                    const float *Z_pool, const int32_t *slot, float *out, void *stream);
+
+/* Commit tokens into the recurrent states (section 3.1, state update):
+ *   S += sum_t phi(k_t) v_t^T,   Z += sum_t phi(k_t)
+ * over the first n_valid[b] of the n_tok tokens passed for request b.
+ * Any n_tok >= 0 is accepted: a block, several blocks, or a whole prefix in
+ * one call; by associativity the result does not depend on the chunking.
+ * Reads: batch, heads, head_dim, feat, in_dtype, n_slots (block is ignored).
+ *   n_valid  [B] int32 or NULL   tokens to fold per request; NULL means n_tok.
+ *                                Precondition: 0 <= n_valid[b] <= n_tok.
+ *   k, v     [B][H][n_tok][d]    in_dtype
+ *   W        [H][d][F]           in_dtype
+ *   S_pool   [n_slots][H][2F][d] fp32, updated in place
+ *   Z_pool   [n_slots][H][2F]    fp32, updated in place
+ *   slot     [B] int32 or NULL   as for hba_step.  Precondition: slots are
+ *                                distinct within one call (each request owns
+ *                                its state; no atomics are used).
+ * The update is deterministic: the same inputs give bitwise-equal states. */
+hba_status hba_commit(const hba_shape *shape, int32_t n_tok, const int32_t *n_valid,
+                      const void *k, const void *v, const void *W, float *S_pool,
+                      float *Z_pool, const int32_t *slot, void *stream);
+
+/* Comparator: full softmax attention (section 2.2) of the active block's
+ * queries over the request's cached prefix followed by the block itself,
+ * scale 1/sqrt(d), every key visible, no gate -- the prefix attention that
+ * block-hybrid attention replaces with a fixed-size state.
+ * Reads: batch, heads, block, head_dim, in_dtype (feat and n_slots ignored).
+ *   prefix_len [B] int32 or NULL  cached tokens used by request b; NULL means
+ *                                 max_prefix.  Precondition:
+ *                                 0 <= prefix_len[b] <= max_prefix.
+ *   q, k, v    [B][H][L][d]       in_dtype, the active block
+ *   Kc, Vc     [B][H][max_prefix][d] in_dtype, the prefix cache; may be NULL
+ *                                 only when max_prefix == 0
+ *   out        [B][H][L][d]       fp32 output */
+hba_status hba_prefix_softmax(const hba_shape *shape, int32_t max_prefix,
+                              const int32_t *prefix_len, const void *q, const void *k,
+                              const void *v, const void *Kc, const void *Vc, float *out,
+                              void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *hba_status_string(hba_status status);
+
+/* Library ABI version, currently 1. */
+int32_t hba_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HBA_H */

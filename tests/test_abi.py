@@ -1,0 +1,144 @@
+"""The C ABI: the library loads, exports every call the header declares, and
+rejects bad arguments on the host before anything reaches a GPU.
+
+Every call here is built so that host validation fails (or the call is an
+explicit no-op), so nothing is ever launched -- the fake pointers below are
+never dereferenced.  Calls with fake pointers are skipped when a GPU is
+present, as a second guard.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import block_hybrid_attention_amd as hba
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hba.h")
+OK, ENULL, ESHAPE, EUNSUP, EDTYPE, EALIGN, ECAP = 0, 1, 2, 3, 4, 5, 6
+no_gpu_only = pytest.mark.skipif(torch.cuda.is_available(),
+                                 reason="fake-pointer validation tests run only without a GPU")
+
+
+def lib():
+    if not os.path.exists(hba.library_path()):
+        import block_hybrid_attention_amd.build as b
+        b.build()
+    return hba.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:hba_status|const char \*|int32_t)\s*\**\s*(hba_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"hba_feature_map", "hba_step", "hba_commit", "hba_prefix_softmax",
+            "hba_status_string", "hba_abi_version"} <= set(names)
+    L = lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert hba.abi_version() == 1
+
+
+def test_status_strings():
+    L = lib()
+    for code in range(8):
+        s = L.hba_status_string(code)
+        assert s and s != b"unknown status"
+    assert L.hba_status_string(99) == b"unknown status"
+
+
+def shape(batch=2, heads=4, block=32, d=128, F=128, dtype=1, slots=8):
+    return hba.Shape(batch, heads, block, d, F, dtype, slots)
+
+
+A = ctypes.c_void_p(0x10000)      # aligned, never dereferenced
+A2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10004)    # 4-byte aligned only
+
+
+def step_call(sh, q=A, k=A, v=A, W=A, gate=None, S=A2, Z=A2, slot=None, out=A2):
+    return lib().hba_step(ctypes.byref(sh) if sh is not None else None, q, k, v, W, gate, S, Z, slot, out, None)
+
+
+@no_gpu_only
+def test_step_validation():
+    assert step_call(None) == ENULL
+    assert step_call(shape(dtype=7)) == EDTYPE
+    assert step_call(shape(d=96)) == EUNSUP
+    assert step_call(shape(F=32)) == EUNSUP
+    assert step_call(shape(block=0)) == ESHAPE
+    assert step_call(shape(block=33)) == EUNSUP
+    assert step_call(shape(heads=0)) == ESHAPE
+    assert step_call(shape(batch=-1)) == ESHAPE
+    assert step_call(shape(slots=-1)) == ESHAPE
+    assert step_call(shape(), q=None) == ENULL
+    assert step_call(shape(), S=None) == ENULL
+    assert step_call(shape(batch=9, slots=8)) == ECAP         # no slot map, too many requests
+    assert step_call(shape(), k=MIS) == EALIGN
+    assert step_call(shape(), out=MIS) == EALIGN
+    assert step_call(shape(), gate=ctypes.c_void_p(0x10001), slot=A) == EALIGN
+
+
+def test_zero_batch_is_a_noop():
+    # batch == 0 returns before touching any pointer, on any machine
+    assert step_call(shape(batch=0), q=None, k=None, v=None, W=None, S=None, Z=None, out=None) == OK
+    L = lib()
+    sh = shape(batch=0)
+    assert L.hba_commit(ctypes.byref(sh), 32, None, None, None, None, None, None, None, None) == OK
+    assert L.hba_prefix_softmax(ctypes.byref(sh), 64, None, None, None, None, None, None, None, None) == OK
+    assert L.hba_feature_map(ctypes.byref(shape()), 0, None, None, None, None) == OK
+
+
+@no_gpu_only
+def test_commit_validation():
+    L = lib()
+
+    def call(sh, n_tok=32, k=A, v=A, W=A, S=A2, Z=A2, n_valid=None, slot=None):
+        return L.hba_commit(ctypes.byref(sh), n_tok, n_valid, k, v, W, S, Z, slot, None)
+
+    assert call(shape(), n_tok=-1) == ESHAPE
+    assert call(shape(), n_tok=0, k=None) == OK               # nothing to fold
+    assert call(shape(d=32)) == EUNSUP
+    assert call(shape(), v=None) == ENULL
+    assert call(shape(batch=9, slots=8)) == ECAP
+    assert call(shape(), Z=MIS) == EALIGN
+    assert call(shape(), n_valid=ctypes.c_void_p(0x10002), slot=A) == EALIGN
+
+
+@no_gpu_only
+def test_prefix_and_feature_map_validation():
+    L = lib()
+
+    def pcall(sh, P=128, Kc=A, Vc=A, out=A2):
+        return L.hba_prefix_softmax(ctypes.byref(sh), P, None, A, A, A, Kc, Vc, out, None)
+
+    assert pcall(shape(), P=-1) == ESHAPE
+    assert pcall(shape(), Kc=None) == ENULL
+    assert pcall(shape(block=40)) == EUNSUP
+    assert pcall(shape(), Vc=MIS) == EALIGN
+    sh = shape()
+    assert L.hba_feature_map(ctypes.byref(sh), -1, A, A, A2, None) == ESHAPE
+    assert L.hba_feature_map(ctypes.byref(sh), 1 << 31, A, A, A2, None) == ESHAPE
+    assert L.hba_feature_map(ctypes.byref(sh), 10, None, A, A2, None) == ENULL
+    assert L.hba_feature_map(ctypes.byref(shape(F=96)), 10, A, A, A2, None) == EUNSUP
+    assert L.hba_feature_map(ctypes.byref(sh), 10, A, MIS, A2, None) == EALIGN
+
+
+def test_python_binding_refuses_host_tensors():
+    # no CPU fallback: host tensors are rejected before any call
+    lib()
+    q = torch.zeros(1, 1, 8, 64)
+    W = torch.zeros(1, 64, 64)
+    S = torch.zeros(1, 1, 128, 64)
+    Z = torch.zeros(1, 1, 128)
+    with pytest.raises(ValueError, match="GPU"):
+        hba.step(q, q, q, W, S, Z)
+    with pytest.raises(ValueError, match="shape"):
+        hba.step(q, q, q, torch.zeros(1, 64, 32), S, Z)
+    with pytest.raises(ValueError, match="dtype"):
+        hba.step(q, q.bfloat16(), q, W, S, Z)
