@@ -1,0 +1,246 @@
+"""Benchmark: block-hybrid attention denoising step, 128 concurrent requests.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload (one hybrid layer): 128 requests, 16 heads, head_dim 128, F = 128
+(phi dim 256), active block 32 tokens, bf16 q/k/v/W ~ N(0,1) / N(0,1/d), fp32
+states S [256][128] and Z [256] per (request, head) built by hba_commit from
+seeded bf16 prefixes of 512..4096 tokens (uniform, whole 32-token blocks).
+
+A timed step is one hba_step over the whole batch (feature map of q, block
+softmax, linear readout of the states, gated shared-normaliser merge), with
+inputs resident in HBM.  Four independent state/input sets (1.3 GB) rotate so
+the 256 MB last-level cache cannot hold the state between steps.
+
+Prints ONE JSON line: query tokens/s (B*L/t_step), the roofline of hba_step
+(algorithmic bytes per launch / mean launch time from HIP events, against the
+8 TB/s HBM peak) and the fp64 oracle's rate on the host cores for a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "active-block query tokens/sec per hybrid layer at B=128; % of HBM peak"
+HBM_PEAK_GBS = 8000.0
+N_SETS = 4
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_serving_b128_traffic.json")
+STEP_SOURCES = ["block_hybrid_attention_amd/csrc/hba_step.hip",
+                "block_hybrid_attention_amd/csrc/hba_device.h"]
+
+
+def step_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in STEP_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def step_bytes(B, H, L, d, F, in_bytes=2) -> int:
+    """Algorithmic HBM bytes of one hba_step launch: each input read once,
+    the output written once (S and Z fp32, q/k/v/W in_dtype, out fp32)."""
+    state = B * H * 2 * F * (d + 1) * 4
+    qkv = 3 * B * H * L * d * in_bytes
+    w = H * d * F * in_bytes
+    out = B * H * L * d * 4
+    return state + qkv + w + out
+
+
+def commit_bytes(B, H, T, d, F, in_bytes=2) -> int:
+    """Algorithmic bytes of one hba_commit: state read + written, k/v/W read."""
+    return 2 * B * H * 2 * F * (d + 1) * 4 + 2 * B * H * T * d * in_bytes + H * d * F * in_bytes
+
+
+def load_traffic(kernel_hash):
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_hash:
+        return None       # counters were taken on an older kernel
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, W, pk_host, pv_host, plen, q, k, v, n_req: int, seconds: float):
+    """fp64 oracle on the host cores: commit (untimed) then step for the first
+    n_req requests of the workload, repeated for about `seconds`."""
+    import numpy as np
+    import oracle
+
+    H, F, d = W.shape[0], W.shape[2], W.shape[1]
+    S0, Z0 = np.zeros((n_req, H, 2 * F, d)), np.zeros((n_req, H, 2 * F))
+    Sr, Zr = oracle.commit(S0, Z0, pk_host, pv_host, W, n_valid=plen[:n_req])
+    qh, kh, vh = (oracle._f64(t[:n_req]) for t in (q, k, v))
+    Wh = oracle._f64(W)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.step(qh, kh, vh, Wh, Sr, Zr)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    L = q.shape[2]
+    return {"value": n_req * L * reps / el, "unit": "query tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": (f"fp64 C oracle step for the first {n_req} of 128 requests (all 16 heads, "
+                       f"states from the oracle's own commit of their seeded prefixes), "
+                       f"{reps} repetitions in {el:.1f} s")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB read + 1 GiB write elementwise kernel (torch.neg) "
+                         "10 times, to calibrate HBM byte counters")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the step shards by request with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_hybrid_attention_amd as hba
+    from block_hybrid_attention_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        n = (1 << 30) // 4
+        x = torch.ones(n, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(10):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "torch.neg fp32", "read_bytes": 4 * n, "write_bytes": 4 * n,
+                          "launches": 10}), flush=True)
+        return
+    c = wl.serving_b128()
+    B, H, L, d, F = c.batch, c.heads, c.block, c.head_dim, c.feat
+    plen = torch.tensor(c.prefix, dtype=torch.int32)
+    Pmax = int(plen.max())
+    g = wl.generator(c.seed, dev)
+    W = wl.feature_weights(H, d, F, c.dtype, g, dev)
+
+    sets = []
+    keep_host = None
+    for s in range(N_SETS):
+        gs = wl.generator(c.seed * 1000 + s, dev)
+        pk = wl.normal((B, H, Pmax, d), 1.0, c.dtype, gs, dev)
+        pv = wl.normal((B, H, Pmax, d), 1.0, c.dtype, gs, dev)
+        S = torch.zeros((B, H, 2 * F, d), device=dev)
+        Z = torch.zeros((B, H, 2 * F), device=dev)
+        hba.commit(pk, pv, W, S, Z, n_valid=plen.to(dev))
+        q, k, v = wl.block_qkv(B, H, L, d, c.dtype, gs, dev)
+        out = torch.empty((B, H, L, d), device=dev)
+        if s == 0 and not args.no_cpu_baseline:
+            n_req = 16
+            keep_host = (pk[:n_req].cpu(), pv[:n_req].cpu())
+        del pk, pv
+        sets.append((q, k, v, S, Z, out))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        q, k, v, S, Z, out = sets[i % N_SETS]
+        hba.step(q, k, v, W, S, Z, out=out)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, one event pair per launch on the launch stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        q, k, v, S, Z, out = sets[i % N_SETS]
+        starts[i].record(stream)
+        hba.step(q, k, v, W, S, Z, out=out)
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    durs_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    ms_per_step = total_ms / args.steps
+    mean_launch_ms = statistics.fmean(durs_ms)
+    q10, q50, q90 = (statistics.quantiles(durs_ms, n=10)[0], statistics.median(durs_ms),
+                     statistics.quantiles(durs_ms, n=10)[-1])
+
+    nbytes = step_bytes(B, H, L, d, F)
+    achieved = nbytes / (mean_launch_ms * 1e-3) / 1e9
+    khash = step_source_hash()
+    traffic = load_traffic(khash)
+
+    # one block commit (32 tokens) for context: state read-modify-write
+    q, k, v, S, Z, out = sets[0]
+    Sc, Zc = S.clone(), Z.clone()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        hba.commit(k, v, W, Sc, Zc)
+    e0.record(stream)
+    reps = 20
+    for _ in range(reps):
+        hba.commit(k, v, W, Sc, Zc)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    commit_us = e0.elapsed_time(e1) / reps * 1e3
+    cbytes = commit_bytes(B, H, L, d, F)
+    del Sc, Zc
+
+    base = None
+    if not args.no_cpu_baseline:
+        q0, k0, v0 = sets[0][0], sets[0][1], sets[0][2]
+        base = cpu_baseline(wl, W, keep_host[0], keep_host[1], plen, q0, k0, v0, 16, args.cpu_seconds)
+
+    tokens = B * L
+    line = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": "serving_b128: 128 requests x 16 heads, d=128, F=128 (phi 256), block 32, "
+                               "prefix 32*U{16..128} tokens committed with hba_commit; one hba_step",
+                   "batch": B, "heads": H, "block": L, "head_dim": d, "feat": F,
+                   "inputs": "bf16 q/k/v/W", "state": "fp32 S,Z", "accumulate": "fp32",
+                   "rotating_sets": N_SETS, "hbm_pct": 100.0 * achieved / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "kernel": "hba_step (step_kernel<bf16,128,128>)",
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "launch_ms": {"mean": mean_launch_ms, "p10": q10, "p50": q50, "p90": q90},
+                     "source_hash": khash},
+        "cpu_baseline": base,
+        "components": {"commit_block_us": commit_us,
+                       "commit_block_GBps": cbytes / (commit_us * 1e-6) / 1e9,
+                       "commit_algorithmic_bytes": cbytes},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -46,6 +46,34 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Reductions over the 16 lanes of a DPP row (lanes 16g .. 16g+15): rotate by
+// 8 and 4 inside the row, then swap within quads; every lane of the row ends
+// with the result.  Pure VALU data movement, no LDS traffic.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppRowRor8 = 0x128, kDppRowRor4 = 0x124, kDppQuadSwap2 = 0x4E, kDppQuadSwap1 = 0xB1;
+
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f<kDppRowRor8>(v));
+    v = fmaxf(v, dpp_f<kDppRowRor4>(v));
+    v = fmaxf(v, dpp_f<kDppQuadSwap2>(v));
+    return fmaxf(v, dpp_f<kDppQuadSwap1>(v));
+}
+__device__ __forceinline__ float row16_min(float v) {
+    v = fminf(v, dpp_f<kDppRowRor8>(v));
+    v = fminf(v, dpp_f<kDppRowRor4>(v));
+    v = fminf(v, dpp_f<kDppQuadSwap2>(v));
+    return fminf(v, dpp_f<kDppQuadSwap1>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<kDppRowRor8>(v);
+    v += dpp_f<kDppRowRor4>(v);
+    v += dpp_f<kDppQuadSwap2>(v);
+    return v + dpp_f<kDppQuadSwap1>(v);
+}
+
 __device__ __forceinline__ floatx4 mfma_f32(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -141,41 +169,77 @@ __device__ __forceinline__ void store_rows(const RowChunks<T, D> &rc, T *__restr
 }
 
 // W [D][F] of one head (global) -> LDS in the layout ProjGeom describes.
+// bf16: each thread owns 8x8 blocks of W; it reads the block's 8 rows
+// (16 B each, coalesced across threads), transposes the block in registers
+// with byte permutes and writes 8 rows of Wt (16 B each).
+// fp32: rows are copied as they are, 16 B per chunk.
 template <typename T, int D, int F>
 struct WChunks {
+    static constexpr bool kBf16 = sizeof(T) == 2;
     static constexpr int EPC = 16 / (int)sizeof(T);
-    static constexpr int N = D * F / EPC / kThreads;
-    uint4 v[N];
+    static constexpr int BLOCKS = kBf16 ? (D / 8) * (F / 8) : 0;
+    // bf16: blocks per thread (>= 1 when the thread owns any) ; fp32: chunks
+    static constexpr int N = kBf16 ? (BLOCKS + kThreads - 1) / kThreads : D * F / EPC / kThreads;
+    uint4 v[kBf16 ? 8 * N : N];
 };
 
 template <typename T, int D, int F>
 __device__ __forceinline__ void load_w(const T *__restrict__ W, WChunks<T, D, F> &wc) {
-    constexpr int EPC = WChunks<T, D, F>::EPC;
+    using C = WChunks<T, D, F>;
+    if constexpr (C::kBf16) {
 #pragma unroll
-    for (int it = 0; it < WChunks<T, D, F>::N; ++it) {
-        const int c = (int)threadIdx.x + it * kThreads;
-        wc.v[it] = *reinterpret_cast<const uint4 *>(W + (int64_t)c * EPC);
+        for (int it = 0; it < C::N; ++it) {
+            int blk = (int)threadIdx.x + it * kThreads;
+            blk = blk < C::BLOCKS ? blk : C::BLOCKS - 1;     // spare threads repeat the last block
+            const int bf = blk % (F / 8), bi = blk / (F / 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                wc.v[8 * it + e] = *reinterpret_cast<const uint4 *>(W + (int64_t)(8 * bi + e) * F + 8 * bf);
+        }
+    } else {
+#pragma unroll
+        for (int it = 0; it < C::N; ++it) {
+            const int c = (int)threadIdx.x + it * kThreads;
+            wc.v[it] = *reinterpret_cast<const uint4 *>(W + (int64_t)c * C::EPC);
+        }
     }
+}
+
+__device__ __forceinline__ uint32_t u4_word(const uint4 &v, int j) {
+    return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
 }
 
 template <typename T, int D, int F>
 __device__ __forceinline__ void store_w(const WChunks<T, D, F> &wc, T *__restrict__ ws) {
     using G = ProjGeom<T, D, F>;
-    constexpr int EPC = WChunks<T, D, F>::EPC;
-    constexpr int CPR = F / EPC;   // chunks per W row
+    using C = WChunks<T, D, F>;
+    if constexpr (C::kBf16) {
 #pragma unroll
-    for (int it = 0; it < WChunks<T, D, F>::N; ++it) {
-        const int c = (int)threadIdx.x + it * kThreads;
-        const int i = c / CPR, f0 = (c % CPR) * EPC;
-        if constexpr (G::kBf16) {
-            // scatter the 8 features of row i into column i of Wt[f][.]
-            const uint32_t w4[4] = {wc.v[it].x, wc.v[it].y, wc.v[it].z, wc.v[it].w};
+        for (int it = 0; it < C::N; ++it) {
+            const int blk = (int)threadIdx.x + it * kThreads;
+            if (blk < C::BLOCKS) {
+                const int bf = blk % (F / 8), bi = blk / (F / 8);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint16_t h = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-                ws[(f0 + e) * G::WLD + i] = h;
+                for (int c = 0; c < 8; ++c) {
+                    // column c of the block = row 8 bf + c of Wt: pairs of rows
+                    // (2j, 2j+1) give word j, taking the low or high halves
+                    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                    uint32_t w[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        w[j] = __builtin_amdgcn_perm(u4_word(wc.v[8 * it + 2 * j + 1], c >> 1),
+                                                     u4_word(wc.v[8 * it + 2 * j], c >> 1), sel);
+                    *reinterpret_cast<uint4 *>(ws + (8 * bf + c) * G::WLD + 8 * bi) =
+                        make_uint4(w[0], w[1], w[2], w[3]);
+                }
             }
-        } else {
+        }
+    } else {
+        constexpr int CPR = F / C::EPC;
+#pragma unroll
+        for (int it = 0; it < C::N; ++it) {
+            const int c = (int)threadIdx.x + it * kThreads;
+            const int i = c / CPR, f0 = (c % CPR) * C::EPC;
             *reinterpret_cast<uint4 *>(ws + i * G::WLD + f0) = wc.v[it];
         }
     }
@@ -214,6 +278,86 @@ __device__ __forceinline__ void project_tile(const T *__restrict__ xs, const T *
 #pragma unroll
         for (int r = 0; r < 4; ++r) us[(16 * mt + 4 * lg + r) * ULD + 16 * nt + li] = acc[r];
     }
+}
+
+// One 16-row tile of u = X W (all F features) for rows row0 .. row0+15 of a
+// staged X tile, computed by one wave.  Accumulator layout: u[nt][r] is
+// u[row0 + 4(l/16) + r][16 nt + l%16].
+template <typename T, int D, int F>
+__device__ __forceinline__ void project_rows16(const T *__restrict__ xs, const T *__restrict__ ws,
+                                               int row0, floatx4 (&u)[F / 16]) {
+    using G = ProjGeom<T, D, F>;
+    const int lane = (int)threadIdx.x & 63;
+    const int li = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int nt = 0; nt < F / 16; ++nt) u[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (G::kBf16) {
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(xs + (row0 + li) * G::XLD + 32 * ks + 8 * lg);
+#pragma unroll
+            for (int nt = 0; nt < F / 16; ++nt) {
+                const bf16x8 b = *reinterpret_cast<const bf16x8 *>(ws + (16 * nt + li) * G::WLD + 32 * ks + 8 * lg);
+                u[nt] = mfma_bf16(a, b, u[nt]);
+            }
+        }
+    } else {
+#pragma unroll 4
+        for (int ks = 0; ks < D / 4; ++ks) {
+            const float a = xs[(row0 + li) * G::XLD + 4 * ks + lg];
+#pragma unroll
+            for (int nt = 0; nt < F / 16; ++nt) u[nt] = mfma_f32(a, ws[(4 * ks + lg) * G::WLD + 16 * nt + li], u[nt]);
+        }
+    }
+}
+
+// Hedgehog feature map on a 16-row tile held in the accumulator layout of
+// project_rows16 ("Retrofitting Linear Attention into Diffusion Language
+// Models", section 3.1): phi = [softmax(u), softmax(-u)] per row.  Each row
+// lives in one 16-lane DPP row, so the max/min/sum reductions are four DPP
+// steps, done for the lane's four rows at once.  On return u holds
+// softmax(u) and un holds softmax(-u), in the same layout.
+template <int F>
+__device__ __forceinline__ void phi_rows16(floatx4 (&u)[F / 16], floatx4 (&un)[F / 16]) {
+    constexpr int NT = F / 16;
+    float mx[4], mn[4], sp[4], sn[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        mx[r] = u[0][r];
+        mn[r] = u[0][r];
+#pragma unroll
+        for (int nt = 1; nt < NT; ++nt) {
+            mx[r] = fmaxf(mx[r], u[nt][r]);
+            mn[r] = fminf(mn[r], u[nt][r]);
+        }
+        mx[r] = row16_max(mx[r]);
+        mn[r] = row16_min(mn[r]);
+        sp[r] = 0.f;
+        sn[r] = 0.f;
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x = u[nt][r];
+            u[nt][r] = fast_exp(x - mx[r]);    // <= 1
+            un[nt][r] = fast_exp(mn[r] - x);   // <= 1
+            sp[r] += u[nt][r];
+            sn[r] += un[nt][r];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        sp[r] = 1.0f / row16_sum(sp[r]);
+        sn[r] = 1.0f / row16_sum(sn[r]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            u[nt][r] *= sp[r];
+            un[nt][r] *= sn[r];
+        }
 }
 
 // Hedgehog feature map of one staged row, computed by one wave

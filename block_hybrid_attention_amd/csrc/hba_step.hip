@@ -9,16 +9,22 @@
 // bandwidth: the fp32 state S (2F x d, 128 KB at F = d = 128) is read once and
 // dominates the bytes.  Design:
 //   * Every wave owns d/4 output columns and streams its column slice of S
-//     for all 2F rows straight into registers at kernel entry, before any
-//     other work, so the whole state read is in flight during the prologue.
-//   * q, k and W go through LDS; u = q W and the block scores q k^T run on
-//     bf16 MFMA (exact products, fp32 accumulation) or fp32 MFMA for fp32
-//     inputs.
+//     through a ring of registers: the first kRing 4-row steps are requested
+//     at kernel entry, and each step consumed in the main loop requests the
+//     step kRing ahead, so ~16 KB per wave stay in flight from the first
+//     instruction to the last.
+//   * q, k and W are staged in LDS (W transposed in registers on the way).
+//     Waves 0 and 1 each own 16 query rows end to end: u = q W and the block
+//     scores on MFMA (bf16 MFMA for bf16 inputs: exact products, fp32
+//     accumulation; fp32 MFMA for fp32 inputs), then phi(q), phi(q).Z and the
+//     softmax weights in the accumulator layout, where a query row sits in
+//     one 16-lane DPP row and every reduction is four DPP steps.
 //   * Per query the exponent shift c_i = max(m_i + ln w, ln lin_den_i) is
 //     applied to both branches, so w exp(s - c) <= 1 and e^{-c} lin_den <= 1.
 //   * Both numerators become ONE contraction
 //       [w e^{s_i - c_i} | e^{-c_i} phi(q_i)]  x  [V ; S]     (K = L + 2F)
-//     on fp32 MFMA, with the shared denominator applied at the store.
+//     on fp32 MFMA; its A operand reuses the LDS of the staged q, k and W.
+//     The shared denominator is applied at the store.
 #include "hba_device.h"
 #include "hba_internal.h"
 
@@ -28,20 +34,26 @@ template <typename T, int D, int F>
 struct StepGeom {
     using P = ProjGeom<T, D, F>;
     static constexpr int KROWS = kRows + 2 * F;   // rows of the merged contraction
-    static constexpr int SLD = 36;                // score tile row stride (floats)
-    // region 1: q tile, k tile, W  -- dead after the projections, then reused
-    // for the merged A operand [KROWS][32] fp32
+    // q tile, k tile and W are dead once waves 0-1 hold u and the scores in
+    // registers; the merged A operand [KROWS][32] fp32 then reuses their LDS
     static constexpr int q_off = 0;
     static constexpr int k_off = P::x_bytes;
     static constexpr int w_off = 2 * P::x_bytes;
-    static constexpr int r1_in = 2 * P::x_bytes + P::w_bytes;
+    static constexpr int in_bytes = 2 * P::x_bytes + P::w_bytes;
     static constexpr int a_bytes = KROWS * 32 * 4;
-    static constexpr int r1 = r1_in > a_bytes ? r1_in : a_bytes;
-    static constexpr int u_off = r1;
-    static constexpr int s_off = u_off + P::u_bytes;
-    static constexpr int den_off = s_off + kRows * SLD * 4;
-    static constexpr int bytes = den_off + kRows * 4;
+    static constexpr int r1 = in_bytes > a_bytes ? in_bytes : a_bytes;
+    static constexpr int den_off = r1;                // shared denominator per query
+    static constexpr int z_off = den_off + kRows * 4;  // Z of this (request, head)
+    static constexpr int bytes = z_off + 2 * F * 4;
 };
+
+// Common exponent shift of both branches for one query (section 3.1 merge):
+// c = max(m + ln w, ln lin_den), floored at -80 so e^{-c} stays finite.
+__device__ __forceinline__ float exp_shift(float m, float lnw, float lin_den) {
+    float c = m + lnw;
+    if (lin_den > 0.f) c = fmaxf(c, __logf(lin_den));
+    return fmaxf(c, -80.f);
+}
 
 // Row k of the merged A operand holds the 32 queries interleaved as
 // (i, i + 16) pairs, XOR-swizzled by k so that both the per-query column
@@ -53,66 +65,81 @@ __device__ __forceinline__ int a_pair(int k, int li) {
     return k * 32 + ((2 * li) ^ (2 * (k & 15)));
 }
 
-// Load n consecutive input elements and widen to fp32.
-template <typename T, int N>
-__device__ __forceinline__ void load_widen(const T *__restrict__ p, float (&o)[N]) {
-    if constexpr (sizeof(T) == 4) {
-        if constexpr (N == 2) {
+// EPL consecutive block values of one row held in the input type; get(e)
+// widens element e to fp32 (exact).  Rows past the block read as zero.
+template <typename T, int EPL>
+struct VRow;
+template <>
+struct VRow<uint16_t, 2> {
+    uint32_t w;
+    __device__ __forceinline__ void load(const uint16_t *p, bool ok) {
+        const uint32_t t = *reinterpret_cast<const uint32_t *>(p);
+        w = ok ? t : 0u;
+    }
+    __device__ __forceinline__ float get(int e) const { return __uint_as_float(e ? (w & 0xffff0000u) : (w << 16)); }
+};
+template <>
+struct VRow<uint16_t, 1> {
+    uint32_t w;
+    __device__ __forceinline__ void load(const uint16_t *p, bool ok) {
+        const uint32_t t = *p;
+        w = ok ? t : 0u;
+    }
+    __device__ __forceinline__ float get(int) const { return __uint_as_float(w << 16); }
+};
+template <int EPL>
+struct VRow<float, EPL> {
+    float f[EPL];
+    __device__ __forceinline__ void load(const float *p, bool ok) {
+        if constexpr (EPL == 2) {
             const float2 t = *reinterpret_cast<const float2 *>(p);
-            o[0] = t.x;
-            o[1] = t.y;
+            f[0] = ok ? t.x : 0.f;
+            f[1] = ok ? t.y : 0.f;
         } else {
-#pragma unroll
-            for (int e = 0; e < N; ++e) o[e] = p[e];
-        }
-    } else {
-        if constexpr (N == 2) {
-            const uint32_t t = *reinterpret_cast<const uint32_t *>(p);
-            o[0] = bf16_bits_to_f32(t & 0xffffu);
-            o[1] = bf16_bits_to_f32(t >> 16);
-        } else {
-#pragma unroll
-            for (int e = 0; e < N; ++e) o[e] = to_f32(p[e]);
+            const float t = *p;
+            f[0] = ok ? t : 0.f;
         }
     }
-}
+    __device__ __forceinline__ float get(int e) const { return f[e]; }
+};
 
-// s = q k^T (unscaled) for the 32x32 block; wave w computes 16x16 tile w.
+// Block scores q k^T (unscaled) for 16 query rows row0.. and all 32 keys,
+// computed by one wave: s[nt][r] = q[row0 + 4(l/16) + r] . k[16 nt + l%16].
 template <typename T, int D, int F>
-__device__ __forceinline__ void block_scores(const T *__restrict__ qs, const T *__restrict__ ks,
-                                             float *__restrict__ ss) {
+__device__ __forceinline__ void block_scores16(const T *__restrict__ qs, const T *__restrict__ ks,
+                                               int row0, floatx4 (&s)[2]) {
     using P = ProjGeom<T, D, F>;
-    using G = StepGeom<T, D, F>;
-    const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
+    const int lane = (int)threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
-    const int mt = wave >> 1, nt = wave & 1;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    s[0] = s[1] = floatx4{0.f, 0.f, 0.f, 0.f};
     if constexpr (P::kBf16) {
 #pragma unroll
         for (int ks_ = 0; ks_ < D / 32; ++ks_) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(qs + (16 * mt + li) * P::XLD + 32 * ks_ + 8 * lg);
-            const bf16x8 b = *reinterpret_cast<const bf16x8 *>(ks + (16 * nt + li) * P::XLD + 32 * ks_ + 8 * lg);
-            acc = mfma_bf16(a, b, acc);
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(qs + (row0 + li) * P::XLD + 32 * ks_ + 8 * lg);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const bf16x8 b = *reinterpret_cast<const bf16x8 *>(ks + (16 * nt + li) * P::XLD + 32 * ks_ + 8 * lg);
+                s[nt] = mfma_bf16(a, b, s[nt]);
+            }
         }
     } else {
-#pragma unroll
+#pragma unroll 4
         for (int ks_ = 0; ks_ < D / 4; ++ks_) {
-            acc = mfma_f32(qs[(16 * mt + li) * P::XLD + 4 * ks_ + lg],
-                           ks[(16 * nt + li) * P::XLD + 4 * ks_ + lg], acc);
+            const float a = qs[(row0 + li) * P::XLD + 4 * ks_ + lg];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) s[nt] = mfma_f32(a, ks[(16 * nt + li) * P::XLD + 4 * ks_ + lg], s[nt]);
         }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ss[(16 * mt + 4 * lg + r) * G::SLD + 16 * nt + li] = acc[r];
 }
 
 template <typename T, int D, int F>
-__global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
-    using P = ProjGeom<T, D, F>;
+__global__ __launch_bounds__(kThreads, 3) void step_kernel(StepArgs a) {
     using G = StepGeom<T, D, F>;
     constexpr int EPL = D / 64;       // columns per lane per MFMA column group
     constexpr int NCOL = D / 4;       // output columns owned by one wave
     constexpr int KS = 2 * F / 4;     // 4-row K-steps over the state
-    constexpr int FM = F / 64;
+    constexpr int RING = KS < 24 ? KS : 24;   // state K-steps kept in flight
+    constexpr int NT = F / 16;        // 16-feature tiles of phi
     constexpr float kScale = D == 128 ? 0.08838834764831845f : 0.125f;   // 1/sqrt(d)
 
     __shared__ __attribute__((aligned(16))) char smem[G::bytes];
@@ -120,9 +147,8 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
     T *ks = reinterpret_cast<T *>(smem + G::k_off);
     T *ws = reinterpret_cast<T *>(smem + G::w_off);
     float *As = reinterpret_cast<float *>(smem);
-    float *us = reinterpret_cast<float *>(smem + G::u_off);
-    float *ss = reinterpret_cast<float *>(smem + G::s_off);
     float *dens = reinterpret_cast<float *>(smem + G::den_off);
+    float *zs = reinterpret_cast<float *>(smem + G::z_off);
 
     const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
@@ -144,13 +170,16 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
     load_rows<T, D>(kg, D, L, kc);
     WChunks<T, D, F> wc;
     load_w<T, D, F>(Wg, wc);
+    constexpr int ZQ = 2 * F / 4;   // float4 chunks of Z
+    float4 zq = make_float4(0.f, 0.f, 0.f, 0.f);
+    if ((int)threadIdx.x < ZQ) zq = reinterpret_cast<const float4 *>(Zg)[threadIdx.x];
 
-    // 2. the state stream: this wave's column slice of S, all 2F rows
+    // 2. open the state stream: the first RING 4-row steps of this wave's slice
     const int c0 = wave * NCOL + EPL * li;
+    const float *sp = Sg + (int64_t)lg * D + c0;
     float sreg[KS][EPL];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        const float *p = Sg + (int64_t)(4 * kk + lg) * D + c0;
+    auto load_s = [&](int kk) {
+        const float *p = sp + (int64_t)(4 * kk) * D;
         if constexpr (EPL == 2) {
             const floatx2 t = __builtin_nontemporal_load(reinterpret_cast<const floatx2 *>(p));
             sreg[kk][0] = t[0];
@@ -158,83 +187,108 @@ __global__ __launch_bounds__(kThreads) void step_kernel(StepArgs a) {
         } else {
             sreg[kk][0] = __builtin_nontemporal_load(p);
         }
-    }
-    // block values (B operand rows 0..31 of the merged contraction)
-    float vreg[8][EPL];
+    };
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-        const int j = 4 * kk + lg;
-        load_widen<T, EPL>(vg + (int64_t)(j < L ? j : L - 1) * D + c0, vreg[kk]);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) vreg[kk][e] = j < L ? vreg[kk][e] : 0.f;
-    }
-    float zr[2 * FM];
-#pragma unroll
-    for (int m = 0; m < 2 * FM; ++m) zr[m] = Zg[lane + 64 * m];
+    for (int kk = 0; kk < RING; ++kk) load_s(kk);
     const float lnw = a.gate ? __logf(a.gate[h]) : 0.f;
 
     // 3. stage q, k, W
     store_rows<T, D, F>(qc, qs);
     store_rows<T, D, F>(kc, ks);
     store_w<T, D, F>(wc, ws);
+    if ((int)threadIdx.x < ZQ) reinterpret_cast<float4 *>(zs)[threadIdx.x] = zq;
     __syncthreads();
 
-    // 4. u = q W and s = q k^T
-    project_tile<T, D, F>(qs, ws, us);
-    block_scores<T, D, F>(qs, ks, ss);
-    __syncthreads();
+    // 4. waves 0-1: u = q W and block scores for query rows 16w .. 16w+15
+    const int row0 = 16 * wave;
+    floatx4 u[NT], sc[2];
+    if (wave < 2) {
+        project_rows16<T, D, F>(qs, ws, row0, u);
+        block_scores16<T, D, F>(qs, ks, row0, sc);
+    }
+    __syncthreads();   // q, k, W are dead: their LDS becomes the A operand
 
-    // 5. per query: phi(q), lin_den, shared shift, merged A operand row
-#pragma unroll 1
-    for (int ii = 0; ii < 8; ++ii) {
-        const int i = 8 * wave + ii;
-        if (i >= L) break;
-        float pp[FM], pn[FM];
-        phi_of_row<F>(us + i * P::ULD, lane, pp, pn);
-        float ld = 0.f;
+    // 5. waves 0-1: per query the shift, block weights and scaled phi(q),
+    //    one of the lane's four rows at a time
+    if (wave < 2) {
 #pragma unroll
-        for (int m = 0; m < FM; ++m) ld += pp[m] * zr[m] + pn[m] * zr[FM + m];
-        const float lin_den = wave_sum(ld);
-        const float sj = lane < L ? ss[i * G::SLD + lane] * kScale : -INFINITY;
-        const float mx = wave_max(sj);
-        float c = mx + lnw;
-        if (lin_den > 0.f) c = fmaxf(c, __logf(lin_den));
-        c = fmaxf(c, -80.f);
-        const float p = lane < L ? fast_exp(sj + lnw - c) : 0.f;
-        const float sm_den = wave_sum(p);
-        const float elin = lin_den > 0.f ? fast_exp(-c) : 0.f;
-        if (lane < 32) As[a_index(lane, i)] = p;
+        for (int r = 0; r < 4; ++r) {
+            const int i = row0 + 4 * lg + r;
+            float mx = u[0][r], mn = u[0][r];
 #pragma unroll
-        for (int m = 0; m < FM; ++m) {
-            As[a_index(kRows + lane + 64 * m, i)] = pp[m] * elin;
-            As[a_index(kRows + F + lane + 64 * m, i)] = pn[m] * elin;
+            for (int nt = 1; nt < NT; ++nt) {
+                mx = fmaxf(mx, u[nt][r]);
+                mn = fminf(mn, u[nt][r]);
+            }
+            mx = row16_max(mx);
+            mn = row16_min(mn);
+            // phi(q) = [softmax(u), softmax(-u)]: sums first, values recomputed
+            float sp_ = 0.f, sn_ = 0.f;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                sp_ += fast_exp(u[nt][r] - mx);
+                sn_ += fast_exp(mn - u[nt][r]);
+            }
+            const float ip = 1.0f / row16_sum(sp_), in_ = 1.0f / row16_sum(sn_);
+            float t = 0.f;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                t += fast_exp(u[nt][r] - mx) * ip * zs[16 * nt + li] +
+                     fast_exp(mn - u[nt][r]) * in_ * zs[F + 16 * nt + li];
+            const float ld = row16_sum(t);   // lin_den = phi(q).Z
+            const float s0 = li < L ? sc[0][r] * kScale : -INFINITY;
+            const float s1 = (16 + li) < L ? sc[1][r] * kScale : -INFINITY;
+            const float m = row16_max(fmaxf(s0, s1));
+            const float c = exp_shift(m, lnw, ld);
+            const float elin = ld > 0.f ? fast_exp(-c) : 0.f;
+            const float p0 = li < L ? fast_exp(s0 + lnw - c) : 0.f;
+            const float p1 = (16 + li) < L ? fast_exp(s1 + lnw - c) : 0.f;
+            As[a_index(li, i)] = p0;
+            As[a_index(16 + li, i)] = p1;
+            const float psum = row16_sum(p0 + p1);
+            if (li == 0) dens[i] = psum + elin * ld;
+            const float ep = ip * elin, en = in_ * elin;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                As[a_index(kRows + 16 * nt + li, i)] = fast_exp(u[nt][r] - mx) * ep;
+                As[a_index(kRows + F + 16 * nt + li, i)] = fast_exp(mn - u[nt][r]) * en;
+            }
         }
-        if (lane == 0) dens[i] = sm_den + elin * lin_den;
     }
     __syncthreads();
 
-    // 6. merged contraction [w P | e^{-c} phi(q)] x [V ; S] on fp32 MFMA
+    // 6. merged contraction [w P | e^{-c} phi(q)] x [V ; S] on fp32 MFMA:
+    //    the state rows first (the stream is already in flight), then the
+    //    block values, requested now and kept in the input type until use
+    VRow<T, EPL> vreg[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        const int j = 4 * kk + lg;
+        vreg[kk].load(vg + (int64_t)(j < L ? j : L - 1) * D + c0, j < L);
+    }
     floatx4 acc[2][EPL];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[t][e] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-        const float2 av = *reinterpret_cast<const float2 *>(As + a_pair(4 * kk + lg, li));
+    for (int kk = 0; kk < KS; ++kk) {
+        if (kk + RING < KS) load_s(kk + RING);   // keep the ring full
+        const floatx2 av = *reinterpret_cast<const floatx2 *>(As + a_pair(kRows + 4 * kk + lg, li));
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-            acc[0][e] = mfma_f32(av.x, vreg[kk][e], acc[0][e]);
-            acc[1][e] = mfma_f32(av.y, vreg[kk][e], acc[1][e]);
+            acc[0][e] = mfma_f32(av[0], sreg[kk][e], acc[0][e]);
+            acc[1][e] = mfma_f32(av[1], sreg[kk][e], acc[1][e]);
         }
     }
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        const float2 av = *reinterpret_cast<const float2 *>(As + a_pair(kRows + 4 * kk + lg, li));
+    for (int kk = 0; kk < 8; ++kk) {
+        const floatx2 av = *reinterpret_cast<const floatx2 *>(As + a_pair(4 * kk + lg, li));
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-            acc[0][e] = mfma_f32(av.x, sreg[kk][e], acc[0][e]);
-            acc[1][e] = mfma_f32(av.y, sreg[kk][e], acc[1][e]);
+            const float bv = vreg[kk].get(e);
+            acc[0][e] = mfma_f32(av[0], bv, acc[0][e]);
+            acc[1][e] = mfma_f32(av[1], bv, acc[1][e]);
         }
     }
 
