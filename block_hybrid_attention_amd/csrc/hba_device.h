@@ -82,9 +82,9 @@ __device__ __forceinline__ floatx4 mfma_bf16(bf16x8 a, bf16x8 b, floatx4 c) {
 }
 
 // exp(x) through the hardware base-2 exponential.
-__device__ __forceinline__ float fast_exp(float x) {
-    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
-}
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
 // LDS geometry of the projection stage, per input element type.
@@ -307,6 +307,37 @@ __device__ __forceinline__ void project_rows16(const T *__restrict__ xs, const T
             const float a = xs[(row0 + li) * G::XLD + 4 * ks + lg];
 #pragma unroll
             for (int nt = 0; nt < F / 16; ++nt) u[nt] = mfma_f32(a, ws[(4 * ks + lg) * G::WLD + 16 * nt + li], u[nt]);
+        }
+    }
+}
+
+// N-tiles nt0 .. nt0+NTW-1 of u = X W for rows row0 .. row0+15 (one wave).
+template <typename T, int D, int F, int NTW>
+__device__ __forceinline__ void project_rows16_part(const T *__restrict__ xs, const T *__restrict__ ws,
+                                                    int row0, int nt0, floatx4 (&u)[NTW]) {
+    using G = ProjGeom<T, D, F>;
+    const int lane = (int)threadIdx.x & 63;
+    const int li = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) u[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (G::kBf16) {
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(xs + (row0 + li) * G::XLD + 32 * ks + 8 * lg);
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const bf16x8 b =
+                    *reinterpret_cast<const bf16x8 *>(ws + (16 * (nt0 + j) + li) * G::WLD + 32 * ks + 8 * lg);
+                u[j] = mfma_bf16(a, b, u[j]);
+            }
+        }
+    } else {
+#pragma unroll 4
+        for (int ks = 0; ks < D / 4; ++ks) {
+            const float a = xs[(row0 + li) * G::XLD + 4 * ks + lg];
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+                u[j] = mfma_f32(a, ws[(4 * ks + lg) * G::WLD + 16 * (nt0 + j) + li], u[j]);
         }
     }
 }
