@@ -184,9 +184,248 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(CommitArgs a) {
     if (tid < 2 * F) Zg[tid] = zacc;
 }
 
+// ---------------------------------------------------------------------------
+// bf16 inputs: two workgroups per (request, head), one per half of the state
+// (rows of softmax(kW) or of softmax(-kW)), four waves each, split-bf16 MFMA.
+//   * W, the k tile and v (transposed, so tokens are contiguous for the MFMA
+//     B operand) are staged in LDS; the 8x8 transposes run in registers.
+//   * Waves 0-1 form u = k W for 16 tokens each (a token row sits in one
+//     16-lane DPP row), then this half of phi(k), written in fp32 to LDS; for
+//     one-block commits that buffer reuses the LDS of W.
+//   * Every wave owns F/4 state rows and adds phi(K)^T V on bf16 MFMA with phi
+//     split into a bf16 high part and residual (v is exact in bf16): two
+//     products per tile.  Each lane owns d/16 consecutive columns, so the
+//     state is read and written in whole 512-byte rows.
+//   * Waves 2-3 sum phi over tokens for Z in fp32, one feature per thread.
+template <int D, int F, bool kResidentW>
+struct CommitGeomBf16 {
+    using P = ProjGeom<uint16_t, D, F>;
+    static constexpr int TP = kRows + 8;         // V^T row stride (bf16): tokens + pad
+    static constexpr int PHLD = F + 2;           // phi-half row stride (floats)
+    static constexpr int k_off = 0;
+    static constexpr int v_off = P::x_bytes;
+    static constexpr int w_off = v_off + D * TP * 2;
+    static constexpr int phi_bytes = kRows * PHLD * 4;
+    static constexpr int phi_off = kResidentW ? w_off + P::w_bytes : w_off;
+    static constexpr int wregion = kResidentW ? P::w_bytes + phi_bytes
+                                              : (P::w_bytes > phi_bytes ? P::w_bytes : phi_bytes);
+    static constexpr int bytes = w_off + wregion;
+};
+
+template <int D, int F, bool kResidentW>
+__global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) {
+    using T = uint16_t;
+    using P = ProjGeom<T, D, F>;
+    using G = CommitGeomBf16<D, F, kResidentW>;
+    constexpr int NE = D / 16;          // N-tiles; lane owns NE consecutive columns
+    constexpr int FW = F / 4;           // state rows per wave (this half has F rows)
+    constexpr int MT = FW / 16;         // M-tiles per wave
+    constexpr int NT = F / 16;
+    constexpr int WBLK = (D / 8) * (F / 8);       // 8x8 blocks of W
+    constexpr int VBLK = (kRows / 8) * (D / 8);   // 8x8 blocks of a v chunk
+    constexpr int KCH = kRows * D / 8;            // 16-byte chunks of a k tile
+    static_assert(WBLK <= kThreads && VBLK <= kThreads && KCH % kThreads == 0, "staging split");
+
+    __shared__ __attribute__((aligned(16))) char smem[G::bytes];
+    T *ks = reinterpret_cast<T *>(smem + G::k_off);
+    T *vt = reinterpret_cast<T *>(smem + G::v_off);
+    T *ws = reinterpret_cast<T *>(smem + G::w_off);
+    float *phs = reinterpret_cast<float *>(smem + G::phi_off);
+
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int half = (int)blockIdx.x & 1;     // 0: softmax(kW) rows, 1: softmax(-kW) rows
+    const int bh = (int)blockIdx.x >> 1;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int T_ = a.T;
+    int nv = a.n_valid ? a.n_valid[b] : T_;
+    nv = nv < 0 ? 0 : (nv > T_ ? T_ : nv);
+    if (nv == 0) return;   // nothing to fold; the state is left untouched
+    const int64_t slot = a.slot ? (int64_t)a.slot[b] : (int64_t)b;
+    const T *kg = static_cast<const T *>(a.k) + (int64_t)bh * T_ * D;
+    const T *vg = static_cast<const T *>(a.v) + (int64_t)bh * T_ * D;
+    const T *Wg = static_cast<const T *>(a.W) + (int64_t)h * D * F;
+    float *Sg = a.S + ((slot * a.H + h) * (int64_t)(2 * F) + (int64_t)half * F) * D;
+    float *Zg = a.Z + (slot * a.H + h) * (int64_t)(2 * F) + half * F;
+    const int f_base = wave * FW;
+
+    // staging of one chunk: W blocks (when needed), v blocks and the k tile
+    auto stage = [&](int t0, int nrows, bool with_w) {
+        uint4 wb[8], vb[8], kb[KCH / kThreads];
+        const bool do_w = with_w && tid < WBLK;
+        const bool do_v = tid < VBLK;
+        if (do_w) {
+            const int bf = tid % (F / 8), bi = tid / (F / 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wb[e] = *reinterpret_cast<const uint4 *>(Wg + (int64_t)(8 * bi + e) * F + 8 * bf);
+        }
+        if (do_v) {
+            const int bc = tid % (D / 8), bt = tid / (D / 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int t = 8 * bt + e;
+                const uint4 x = *reinterpret_cast<const uint4 *>(vg + (int64_t)(t0 + (t < nrows ? t : nrows - 1)) * D + 8 * bc);
+                vb[e] = t < nrows ? x : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < KCH / kThreads; ++it) {
+            const int c = tid + it * kThreads;
+            const int kr = c / (D / 8), kc = (c % (D / 8)) * 8;
+            const uint4 x = *reinterpret_cast<const uint4 *>(kg + (int64_t)(t0 + (kr < nrows ? kr : nrows - 1)) * D + kc);
+            kb[it] = kr < nrows ? x : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int it = 0; it < KCH / kThreads; ++it) {
+            const int c = tid + it * kThreads;
+            const int kr = c / (D / 8), kc = (c % (D / 8)) * 8;
+            *reinterpret_cast<uint4 *>(ks + kr * P::XLD + kc) = kb[it];
+        }
+        // 8x8 transposes in registers: output row c of a block = its column c
+        if (do_w) {
+            const int bf = tid % (F / 8), bi = tid / (F / 8);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                uint32_t w[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    w[j] = __builtin_amdgcn_perm(u4_word(wb[2 * j + 1], c >> 1), u4_word(wb[2 * j], c >> 1), sel);
+                *reinterpret_cast<uint4 *>(ws + (8 * bf + c) * P::WLD + 8 * bi) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+        if (do_v) {
+            const int bc = tid % (D / 8), bt = tid / (D / 8);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int col = 8 * bc + c;
+                const int rho = (col % NE) * 16 + col / NE;   // N-tile col%NE, lane col/NE
+                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                uint32_t w[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    w[j] = __builtin_amdgcn_perm(u4_word(vb[2 * j + 1], c >> 1), u4_word(vb[2 * j], c >> 1), sel);
+                *reinterpret_cast<uint4 *>(vt + rho * G::TP + 8 * bt) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    };
+
+    // the old state goes straight into the accumulators: row
+    // f_base + 16 mt + 4 lg + r of this half, columns NE li .. NE li + NE - 1.
+    // Multi-chunk commits load it at entry; a one-block commit loads it once
+    // phi is in LDS, so the accumulators are not live during the prologue.
+    floatx4 acc[MT][NE];
+    auto load_state = [&]() {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float *p = Sg + (int64_t)(f_base + 16 * mt + 4 * lg + r) * D + NE * li;
+#pragma unroll
+                for (int q = 0; q < NE / 4; ++q) {
+                    const float4 t = reinterpret_cast<const float4 *>(p)[q];
+                    acc[mt][4 * q + 0][r] = t.x;
+                    acc[mt][4 * q + 1][r] = t.y;
+                    acc[mt][4 * q + 2][r] = t.z;
+                    acc[mt][4 * q + 3][r] = t.w;
+                }
+            }
+    };
+    if constexpr (kResidentW) load_state();
+    const int zf = tid - 128;   // waves 2-3: one feature each for the Z sums
+    float zacc = (zf >= 0 && zf < F) ? Zg[zf] : 0.f;
+
+#pragma unroll 1
+    for (int t0 = 0; t0 < nv; t0 += kRows) {
+        const int nrows = nv - t0 < kRows ? nv - t0 : kRows;
+        stage(t0, nrows, !kResidentW || t0 == 0);
+        __syncthreads();
+        // waves 0-1: u = k W for tokens 16w .. 16w+15 (log2 domain), and the
+        // max (or min) and sum of this half's softmax per token
+        floatx4 u[NT];
+        float mref[4], inv[4];
+        if (wave < 2) {
+            project_rows16<T, D, F>(ks, ws, 16 * wave, u);
+            const float sgn = half ? -1.f : 1.f;   // phi half = softmax(sgn * u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float m0 = -INFINITY;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    u[nt][r] *= sgn * kLog2e;
+                    m0 = fmaxf(m0, u[nt][r]);
+                }
+                mref[r] = row16_max(m0);
+                float s0 = 0.f;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) s0 += fast_exp2(u[nt][r] - mref[r]);
+                const bool ok = (16 * wave + 4 * lg + r) < nrows;   // rows past the end: phi = 0
+                inv[r] = ok ? 1.0f / row16_sum(s0) : 0.f;
+            }
+        }
+        __syncthreads();   // k tile and W reads done (phi may reuse W's LDS)
+        if (wave < 2) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float *row = phs + (16 * wave + 4 * lg + r) * G::PHLD;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) row[16 * nt + li] = fast_exp2(u[nt][r] - mref[r]) * inv[r];
+            }
+        }
+        if constexpr (!kResidentW) load_state();
+        __syncthreads();
+        if (zf >= 0 && zf < F) {
+            float zs = 0.f;
+#pragma unroll 8
+            for (int i = 0; i < kRows; ++i) zs += phs[i * G::PHLD + zf];
+            zacc += zs;
+        }
+        // S += phi^T V on bf16 MFMA: A[f][t] = phi_f(k_t) (high + residual), B[t][col] = v_t[col]
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            bf16x8 ah, al;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float x = phs[(8 * lg + t) * G::PHLD + f_base + 16 * mt + li];
+                const __bf16 hx = (__bf16)x;
+                ah[t] = hx;
+                al[t] = (__bf16)(x - (float)hx);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NE; ++nt) {
+                const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(vt + (16 * nt + li) * G::TP + 8 * lg);
+                acc[mt][nt] = mfma_bf16(ah, bv, acc[mt][nt]);
+                acc[mt][nt] = mfma_bf16(al, bv, acc[mt][nt]);
+            }
+        }
+        __syncthreads();   // the next chunk reuses every staging buffer
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float *p = Sg + (int64_t)(f_base + 16 * mt + 4 * lg + r) * D + NE * li;
+#pragma unroll
+            for (int q = 0; q < NE / 4; ++q)
+                reinterpret_cast<float4 *>(p)[q] = make_float4(acc[mt][4 * q + 0][r], acc[mt][4 * q + 1][r],
+                                                                acc[mt][4 * q + 2][r], acc[mt][4 * q + 3][r]);
+        }
+    if (zf >= 0 && zf < F) Zg[zf] = zacc;
+}
+
 template <typename T, int D, int F>
 static hipError_t launch_commit_t(const CommitArgs &a, hipStream_t stream) {
-    return launch_kernel(commit_kernel<T, D, F>, dim3((unsigned)(a.B * a.H)), dim3(kThreads), a, stream);
+    const dim3 grid((unsigned)(a.B * a.H));
+    if constexpr (sizeof(T) == 2) {
+        const dim3 grid2((unsigned)(2 * a.B * a.H));   // one workgroup per state half
+        if (a.T <= kRows)   // one block: phi reuses the LDS of W
+            return launch_kernel(commit_kernel_bf16<D, F, false>, grid2, dim3(kThreads), a, stream);
+        return launch_kernel(commit_kernel_bf16<D, F, true>, grid2, dim3(kThreads), a, stream);
+    } else {
+        return launch_kernel(commit_kernel<T, D, F>, grid, dim3(kThreads), a, stream);
+    }
 }
 
 hipError_t launch_commit(const CommitArgs &a, bool bf16, int d, int F, hipStream_t stream) {

@@ -283,7 +283,9 @@ __device__ __forceinline__ void project_tile(const T *__restrict__ xs, const T *
 // One 16-row tile of u = X W (all F features) for rows row0 .. row0+15 of a
 // staged X tile, computed by one wave.  Accumulator layout: u[nt][r] is
 // u[row0 + 4(l/16) + r][16 nt + l%16].
-template <typename T, int D, int F>
+// kUnrollK = false keeps one K-step's operands live at a time (less register
+// pressure, more LDS latency exposed).
+template <typename T, int D, int F, bool kUnrollK = true>
 __device__ __forceinline__ void project_rows16(const T *__restrict__ xs, const T *__restrict__ ws,
                                                int row0, floatx4 (&u)[F / 16]) {
     using G = ProjGeom<T, D, F>;
@@ -292,7 +294,7 @@ __device__ __forceinline__ void project_rows16(const T *__restrict__ xs, const T
 #pragma unroll
     for (int nt = 0; nt < F / 16; ++nt) u[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
     if constexpr (G::kBf16) {
-#pragma unroll
+#pragma unroll (kUnrollK ? D / 32 : 1)
         for (int ks = 0; ks < D / 32; ++ks) {
             const bf16x8 a = *reinterpret_cast<const bf16x8 *>(xs + (row0 + li) * G::XLD + 32 * ks + 8 * lg);
 #pragma unroll
