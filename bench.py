@@ -1,6 +1,8 @@
 """Benchmark: block-hybrid attention denoising step, 128 concurrent requests.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --comparator     # hybrid step vs full softmax over P-token caches
+    python bench.py --decode-loop    # B=32 decode loop: 8 steps + 1 commit per block
 
 Workload (one hybrid layer): 128 requests, 16 heads, head_dim 128, F = 128
 (phi dim 256), active block 32 tokens, bf16 q/k/v/W ~ N(0,1) / N(0,1/d), fp32
@@ -98,6 +100,94 @@ def cpu_baseline(wl, W, pk_host, pv_host, plen, q, k, v, n_req: int, seconds: fl
                        f"{reps} repetitions in {el:.1f} s")}
 
 
+def _time_launches(torch, fn, warmup, iters, stream):
+    """Mean and median per-launch time (ms) from HIP events on the launch stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    en = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    for i in range(iters):
+        st[i].record(stream)
+        fn()
+        en[i].record(stream)
+    torch.cuda.synchronize()
+    d = [a.elapsed_time(b) for a, b in zip(st, en)]
+    return statistics.fmean(d), statistics.median(d)
+
+
+def comparator_sweep(args, torch, hba, wl, dev):
+    """Full softmax attention over a P-token bf16 KV cache (the layer the
+    hybrid replaces) against the hybrid step reading the fixed-size state
+    built from the same cache: 128 requests, 16 heads, d=128, block 32."""
+    B, H, L, d, F = 128, 16, 32, 128, 128
+    dt = torch.bfloat16
+    stream = torch.cuda.current_stream()
+    rows = []
+    for P in wl.COMPARATOR_PREFIXES:
+        g = wl.generator(5_000_000 + P, dev)
+        W = wl.feature_weights(H, d, F, dt, g, dev)
+        Kc = wl.normal((B, H, P, d), 1.0, dt, g, dev)
+        Vc = wl.normal((B, H, P, d), 1.0, dt, g, dev)
+        q, k, v = wl.block_qkv(B, H, L, d, dt, g, dev)
+        S = torch.zeros((B, H, 2 * F, d), device=dev)
+        Z = torch.zeros((B, H, 2 * F), device=dev)
+        hba.commit(Kc, Vc, W, S, Z)
+        out_c = torch.empty((B, H, L, d), device=dev)
+        out_h = torch.empty((B, H, L, d), device=dev)
+        n = max(3, min(args.steps, 20 if P >= 16384 else 50))
+        cm, cmed = _time_launches(torch, lambda: hba.prefix_softmax(q, k, v, Kc, Vc, out=out_c), 2, n, stream)
+        hm, hmed = _time_launches(torch, lambda: hba.step(q, k, v, W, S, Z, out=out_h), 3, n, stream)
+        kv_bytes = 2 * B * H * P * d * 2
+        c_bytes = kv_bytes + 3 * B * H * L * d * 2 + B * H * L * d * 4
+        rows.append({"prefix": P, "comparator_ms": cm, "comparator_median_ms": cmed,
+                     "comparator_GBps": c_bytes / (cm * 1e-3) / 1e9,
+                     "hybrid_ms": hm, "hybrid_median_ms": hmed,
+                     "hybrid_GBps": step_bytes(B, H, L, d, F) / (hm * 1e-3) / 1e9,
+                     "speedup": cm / hm, "comparator_kv_bytes": kv_bytes})
+        del Kc, Vc, S, Z
+        torch.cuda.empty_cache()
+    print(json.dumps({"mode": "comparator_sweep", "batch": B, "heads": H, "block": L, "head_dim": d,
+                      "feat": F, "dtype": "bf16 inputs, fp32 accumulate", "unit": "ms per 32-token block",
+                      "rows": rows}), flush=True)
+
+
+def decode_loop(args, torch, hba, wl, dev):
+    """One hybrid layer through a block-diffusion decode: per 32-token block,
+    8 denoising steps (hba_step) then hba_commit of the block; 32 requests."""
+    B, H, L, d, F, nsteps = 32, 16, 32, 128, 128, 8
+    dt = torch.bfloat16
+    stream = torch.cuda.current_stream()
+    W = wl.feature_weights(H, d, F, dt, wl.generator(wl.DECODE_B32_SEED - 1, dev), dev)
+    pool = [wl.block_qkv(B, H, L, d, dt, wl.generator(wl.DECODE_B32_SEED + i, dev), dev) for i in range(16)]
+    S = torch.zeros((B, H, 2 * F, d), device=dev)
+    Z = torch.zeros((B, H, 2 * F), device=dev)
+    out = torch.empty((B, H, L, d), device=dev)
+
+    def block(n):
+        for s_ in range(nsteps):
+            q, k, v = pool[(n * nsteps + s_) % len(pool)]
+            hba.step(q, k, v, W, S, Z, out=out)
+        hba.commit(k, v, W, S, Z)
+
+    for n in range(2):
+        block(n)
+    S.zero_()
+    Z.zero_()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for n in range(args.blocks):
+        block(n)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    print(json.dumps({"mode": "decode_loop", "batch": B, "heads": H, "block": L, "steps_per_block": nsteps,
+                      "blocks": args.blocks, "total_ms": ms, "us_per_block": ms * 1e3 / args.blocks,
+                      "generated_tokens_per_s": B * L * args.blocks / (ms * 1e-3),
+                      "query_tokens_per_s": B * L * nsteps * args.blocks / (ms * 1e-3)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,6 +195,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--comparator", action="store_true",
+                    help="time hba_prefix_softmax against hba_step at B=128 for P = 1k/4k/16k/32k")
+    ap.add_argument("--decode-loop", action="store_true",
+                    help="time the B=32 decode loop (8 steps + 1 commit per 32-token block)")
+    ap.add_argument("--blocks", type=int, default=256)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel (torch.neg) "
                          "10 times, to calibrate HBM byte counters")
@@ -130,6 +225,10 @@ def main():
         print(json.dumps({"calibration": "torch.neg fp32", "read_bytes": 4 * n, "write_bytes": 4 * n,
                           "launches": 10}), flush=True)
         return
+    if args.comparator:
+        return comparator_sweep(args, torch, hba, wl, dev)
+    if args.decode_loop:
+        return decode_loop(args, torch, hba, wl, dev)
     c = wl.serving_b128()
     B, H, L, d, F = c.batch, c.heads, c.block, c.head_dim, c.feat
     plen = torch.tensor(c.prefix, dtype=torch.int32)
