@@ -2,7 +2,7 @@
 // and dispatch to the gfx950 kernels.  Nothing here allocates device memory
 // or synchronises; every call enqueues at most one kernel on the caller's
 // stream.
-#include "../../include/hba.h"
+#include "hba.h"
 
 #include <hip/hip_runtime.h>
 

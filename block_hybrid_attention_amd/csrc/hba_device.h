@@ -19,6 +19,7 @@ namespace hba {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kThreads = 256;   // 4 waves per workgroup
@@ -29,6 +30,19 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
 }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_bits_to_f32(x); }
+
+// Two floats -> two bf16 (round to nearest even) packed in one word, one
+// v_cvt_pk_bf16_f32; a lands in the low half.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){a, b}, bf16x2));
+}
+// Split two floats into packed bf16 high parts and packed bf16 residuals:
+// x = hi + lo + O(2^-17 |x|).
+__device__ __forceinline__ void split_pk_bf16(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = cvt_pk_bf16(a, b);
+    const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xffff0000u);
+    lo = cvt_pk_bf16(a - ha, b - hb);
+}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

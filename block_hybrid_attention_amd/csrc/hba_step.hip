@@ -386,10 +386,6 @@ struct StepGeomBf16 {
     static constexpr int bytes = row_off + 3 * kRows * 4;
 };
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo_elem, float hi_elem) {
-    const __bf16 a = (__bf16)lo_elem, b = (__bf16)hi_elem;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
 // x = hi + lo with hi = bf16(x) and lo = bf16(x - hi)
 __device__ __forceinline__ float bf16_residual(float x) {
     return x - (float)(__bf16)x;
@@ -403,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 3) void step_kernel_bf16(StepArgs a) {
     constexpr int EPL = D / 64;       // columns per lane per N-tile
     constexpr int NCOL = D / 4;       // output columns owned by one wave
     constexpr int NCH = 2 * F / 32;   // 32-row chunks of the state
-    constexpr int RING = NCH < 3 ? NCH : 3;   // chunks in flight
+    constexpr int RING = NCH < 2 ? NCH : 2;   // chunks in flight
     constexpr int NT = F / 16;        // 16-feature tiles of u^T
     constexpr float kS2 = (D == 128 ? 0.08838834764831845f : 0.125f) * kLog2e;   // log2(e)/sqrt(d)
 
@@ -538,14 +534,15 @@ __global__ __launch_bounds__(kThreads, 3) void step_kernel_bf16(StepArgs a) {
                 en[r] = fast_exp2(mn - acc[m][r]) * in_;  // softmax(-u)_f
                 zd += ep[r] * zp[r] + en[r] * zn[r];
             }
-            *reinterpret_cast<uint2 *>(ah + 16 * m) = make_uint2(pack_bf16x2(ep[0], ep[1]), pack_bf16x2(ep[2], ep[3]));
-            *reinterpret_cast<uint2 *>(al + 16 * m) =
-                make_uint2(pack_bf16x2(bf16_residual(ep[0]), bf16_residual(ep[1])),
-                           pack_bf16x2(bf16_residual(ep[2]), bf16_residual(ep[3])));
-            *reinterpret_cast<uint2 *>(ah + F + 16 * m) = make_uint2(pack_bf16x2(en[0], en[1]), pack_bf16x2(en[2], en[3]));
-            *reinterpret_cast<uint2 *>(al + F + 16 * m) =
-                make_uint2(pack_bf16x2(bf16_residual(en[0]), bf16_residual(en[1])),
-                           pack_bf16x2(bf16_residual(en[2]), bf16_residual(en[3])));
+            uint32_t hp[2], lp[2], hn[2], ln[2];
+            split_pk_bf16(ep[0], ep[1], hp[0], lp[0]);
+            split_pk_bf16(ep[2], ep[3], hp[1], lp[1]);
+            split_pk_bf16(en[0], en[1], hn[0], ln[0]);
+            split_pk_bf16(en[2], en[3], hn[1], ln[1]);
+            *reinterpret_cast<uint2 *>(ah + 16 * m) = make_uint2(hp[0], hp[1]);
+            *reinterpret_cast<uint2 *>(al + 16 * m) = make_uint2(lp[0], lp[1]);
+            *reinterpret_cast<uint2 *>(ah + F + 16 * m) = make_uint2(hn[0], hn[1]);
+            *reinterpret_cast<uint2 *>(al + F + 16 * m) = make_uint2(ln[0], ln[1]);
         }
         zd += __shfl_xor(zd, 16, kWave);
         zd += __shfl_xor(zd, 32, kWave);
@@ -587,21 +584,22 @@ __global__ __launch_bounds__(kThreads, 3) void step_kernel_bf16(StepArgs a) {
         const int j = 8 * lg + t;
         const T *p = vg + (int64_t)(j < L ? j : L - 1) * D + c0;
         const uint32_t w_ = EPL == 2 ? *reinterpret_cast<const uint32_t *>(p) : (uint32_t)*p;
-        vw[t] = j < L ? w_ : 0u;
+        vw[t] = w_;   // keys j >= L carry probability exactly 0
     }
+    __builtin_amdgcn_sched_barrier(0);   // issue the block values before the stream is consumed
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         if (c + RING < NCH) load_chunk(c + RING);
+        __builtin_amdgcn_sched_barrier(0);   // the refill stays ahead of the waits for chunk c
         bf16x8 bh_[EPL], bl_[EPL];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e)
+        for (int e = 0; e < EPL; ++e) {
+            uint32_t hw[4], lw[4];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const float x = sreg[c][t][e];
-                const __bf16 hx = (__bf16)x;
-                bh_[e][t] = hx;
-                bl_[e][t] = (__bf16)(x - (float)hx);
-            }
+            for (int j = 0; j < 4; ++j) split_pk_bf16(sreg[c][2 * j][e], sreg[c][2 * j + 1][e], hw[j], lw[j]);
+            bh_[e] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+            bl_[e] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        }
         const int k0 = kRows + 32 * c + 8 * lg;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
@@ -653,12 +651,12 @@ __global__ __launch_bounds__(kThreads, 3) void step_kernel_bf16(StepArgs a) {
                 c = fmaxf(c, -120.f);
                 const float sv = fast_exp2(g2 - c);
                 const float ss = ld > 0.f ? fast_exp2(-c) : 0.f;
-                const float inv = 1.0f / (sv * as + ss * ld);
+                const float inv = __builtin_amdgcn_rcpf(sv * as + ss * ld);
                 float *o = og + (int64_t)i * D + c0;
                 if constexpr (EPL == 2) {
-                    *reinterpret_cast<float2 *>(o) =
-                        make_float2((sv * accV[mt][0][r] + ss * accS[mt][0][r]) * inv,
-                                    (sv * accV[mt][1][r] + ss * accS[mt][1][r]) * inv);
+                    __builtin_nontemporal_store(floatx2{(sv * accV[mt][0][r] + ss * accS[mt][0][r]) * inv,
+                                                        (sv * accV[mt][1][r] + ss * accS[mt][1][r]) * inv},
+                                                reinterpret_cast<floatx2 *>(o));
                 } else {
                     o[0] = (sv * accV[mt][0][r] + ss * accS[mt][0][r]) * inv;
                 }
