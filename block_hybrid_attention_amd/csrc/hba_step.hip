@@ -400,6 +400,7 @@ __global__ __launch_bounds__(kThreads, 3) void step_kernel_bf16(StepArgs a) {
     constexpr int NCOL = D / 4;       // output columns owned by one wave
     constexpr int NCH = 2 * F / 32;   // 32-row chunks of the state
     constexpr int RING = NCH < 2 ? NCH : 2;   // chunks in flight
+    constexpr int PRE = NCH < 4 ? NCH : 4;    // chunks requested before the contraction
     constexpr int NT = F / 16;        // 16-feature tiles of u^T
     constexpr float kS2 = (D == 128 ? 0.08838834764831845f : 0.125f) * kLog2e;   // log2(e)/sqrt(d)
 
@@ -466,6 +467,10 @@ __global__ __launch_bounds__(kThreads, 3) void step_kernel_bf16(StepArgs a) {
     store_w<T, D, F>(wc, ws);
     if ((int)threadIdx.x < ZQ) reinterpret_cast<float4 *>(zs)[threadIdx.x] = zq;
     __syncthreads();
+    // more of the stream goes out while the prologue computes
+#pragma unroll
+    for (int c = RING; c < PRE; ++c) load_chunk(c);
+    __builtin_amdgcn_sched_barrier(0);
 
     // 4. waves 0-1: u^T = W^T q^T for queries 16w .. 16w+15 (all F features):
     //    acc[m][r] = u[16w + l%16][16m + 4(l/16) + r].
@@ -589,7 +594,7 @@ __global__ __launch_bounds__(kThreads, 3) void step_kernel_bf16(StepArgs a) {
     __builtin_amdgcn_sched_barrier(0);   // issue the block values before the stream is consumed
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-        if (c + RING < NCH) load_chunk(c + RING);
+        if (c + RING < NCH && c + RING >= PRE) load_chunk(c + RING);
         __builtin_amdgcn_sched_barrier(0);   // the refill stays ahead of the waits for chunk c
         bf16x8 bh_[EPL], bl_[EPL];
 #pragma unroll
