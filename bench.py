@@ -15,8 +15,8 @@ inputs resident in HBM.  Four independent state/input sets (1.3 GB) rotate so
 the 256 MB last-level cache cannot hold the state between steps.
 
 Prints ONE JSON line: query tokens/s (B*L/t_step), the roofline of hba_step
-(algorithmic bytes per launch / mean launch time from HIP events, against the
-8 TB/s HBM peak) and the fp64 oracle's rate on the host cores for a bounded
+(algorithmic bytes per launch / mean launch time, i.e. K back-to-back launches
+between two HIP events on the launch stream, against the 8 TB/s HBM peak) and the fp64 oracle's rate on the host cores for a bounded
 sample of the same workload.
 """
 from __future__ import annotations
@@ -101,19 +101,19 @@ def cpu_baseline(wl, W, pk_host, pv_host, plen, q, k, v, n_req: int, seconds: fl
 
 
 def _time_launches(torch, fn, warmup, iters, stream):
-    """Mean and median per-launch time (ms) from HIP events on the launch stream."""
+    """Mean time per launch (ms): `iters` back-to-back launches bracketed by
+    two HIP events on the launch stream (an event pair around every launch
+    would put its own packets between the kernels)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    st = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
-    en = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
-    for i in range(iters):
-        st[i].record(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
         fn()
-        en[i].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    d = [a.elapsed_time(b) for a, b in zip(st, en)]
-    return statistics.fmean(d), statistics.median(d)
+    return e0.elapsed_time(e1) / iters
 
 
 def comparator_sweep(args, torch, hba, wl, dev):
@@ -136,13 +136,13 @@ def comparator_sweep(args, torch, hba, wl, dev):
         out_c = torch.empty((B, H, L, d), device=dev)
         out_h = torch.empty((B, H, L, d), device=dev)
         n = max(3, min(args.steps, 20 if P >= 16384 else 50))
-        cm, cmed = _time_launches(torch, lambda: hba.prefix_softmax(q, k, v, Kc, Vc, out=out_c), 2, n, stream)
-        hm, hmed = _time_launches(torch, lambda: hba.step(q, k, v, W, S, Z, out=out_h), 3, n, stream)
+        cm = _time_launches(torch, lambda: hba.prefix_softmax(q, k, v, Kc, Vc, out=out_c), 2, n, stream)
+        hm = _time_launches(torch, lambda: hba.step(q, k, v, W, S, Z, out=out_h), 3, n, stream)
         kv_bytes = 2 * B * H * P * d * 2
         c_bytes = kv_bytes + 3 * B * H * L * d * 2 + B * H * L * d * 4
-        rows.append({"prefix": P, "comparator_ms": cm, "comparator_median_ms": cmed,
+        rows.append({"prefix": P, "comparator_ms": cm,
                      "comparator_GBps": c_bytes / (cm * 1e-3) / 1e9,
-                     "hybrid_ms": hm, "hybrid_median_ms": hmed,
+                     "hybrid_ms": hm,
                      "hybrid_GBps": step_bytes(B, H, L, d, F) / (hm * 1e-3) / 1e9,
                      "speedup": cm / hm, "comparator_kv_bytes": kv_bytes})
         del Kc, Vc, S, Z
@@ -182,10 +182,56 @@ def decode_loop(args, torch, hba, wl, dev):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
+    final_eager = (S.clone(), Z.clone(), out.clone())
+
+    # The same loop replayed from a HIP graph of two blocks (the input pool
+    # repeats every two blocks), starting from the same zero state.  The
+    # state is cleared outside the graph.  Replays are checked against the
+    # eager loop after 2 and 4 blocks (with eager work and synchronisation
+    # between the replays) and after the full loop.
+    def eager_from_zero(nblocks):
+        S.zero_()
+        Z.zero_()
+        for n in range(nblocks):
+            block(n)
+        torch.cuda.synchronize()
+        return S.clone(), Z.clone(), out.clone()
+
+    def same(a, b):
+        return all(bool(torch.equal(x, y)) for x, y in zip(a, b))
+
+    ref2, ref4 = eager_from_zero(2), eager_from_zero(4)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        block(0)
+        block(1)
+    S.zero_()
+    Z.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    ok = same((S, Z, out), ref2)
+    _ = float(out.abs().sum())   # eager work between replays
+    graph.replay()
+    torch.cuda.synchronize()
+    ok = ok and same((S, Z, out), ref4)
+    reps = args.blocks // 2
+    S.zero_()
+    Z.zero_()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_g = e0.elapsed_time(e1)
+    ok = ok and (2 * reps != args.blocks or same((S, Z, out), final_eager))
     print(json.dumps({"mode": "decode_loop", "batch": B, "heads": H, "block": L, "steps_per_block": nsteps,
                       "blocks": args.blocks, "total_ms": ms, "us_per_block": ms * 1e3 / args.blocks,
                       "generated_tokens_per_s": B * L * args.blocks / (ms * 1e-3),
-                      "query_tokens_per_s": B * L * nsteps * args.blocks / (ms * 1e-3)}), flush=True)
+                      "query_tokens_per_s": B * L * nsteps * args.blocks / (ms * 1e-3),
+                      "graph": {"blocks": 2 * reps, "us_per_block": ms_g * 1e3 / (2 * reps),
+                                "generated_tokens_per_s": B * L * 2 * reps / (ms_g * 1e-3),
+                                "matches_eager": ok}}), flush=True)
 
 
 def main():
@@ -260,26 +306,20 @@ def main():
         hba.step(q, k, v, W, S, Z, out=out)
     torch.cuda.synchronize()
 
-    # timed region: K steps, one event pair per launch on the launch stream
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # timed region: K back-to-back steps bracketed by two HIP events on the
+    # launch stream; the mean launch duration is total / K
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_begin.record(stream)
     for i in range(args.steps):
         q, k, v, S, Z, out = sets[i % N_SETS]
-        starts[i].record(stream)
         hba.step(q, k, v, W, S, Z, out=out)
-        ends[i].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_begin.elapsed_time(t_end)
-    durs_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     ms_per_step = total_ms / args.steps
-    mean_launch_ms = statistics.fmean(durs_ms)
-    q10, q50, q90 = (statistics.quantiles(durs_ms, n=10)[0], statistics.median(durs_ms),
-                     statistics.quantiles(durs_ms, n=10)[-1])
+    mean_launch_ms = ms_per_step
 
     nbytes = step_bytes(B, H, L, d, F)
     achieved = nbytes / (mean_launch_ms * 1e-3) / 1e9
@@ -331,7 +371,8 @@ def main():
                      "traffic": traffic,
                      "kernel": "hba_step (step_kernel<bf16,128,128>)",
                      "algorithmic_bytes_per_launch": nbytes,
-                     "launch_ms": {"mean": mean_launch_ms, "p10": q10, "p50": q50, "p90": q90},
+                     "launch_ms": {"mean": mean_launch_ms,
+                                   "timing": "K back-to-back launches between two HIP events on the launch stream"},
                      "source_hash": khash},
         "cpu_baseline": base,
         "components": {"commit_block_us": commit_us,
