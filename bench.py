@@ -306,20 +306,31 @@ def main():
         hba.step(q, k, v, W, S, Z, out=out)
     torch.cuda.synchronize()
 
-    # timed region: K back-to-back steps bracketed by two HIP events on the
-    # launch stream; the mean launch duration is total / K
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # timed region: K back-to-back steps on the launch stream, with a HIP
+    # event between segments of about K/20 launches (never between every
+    # launch: those packets would sit between the kernels).  The mean launch
+    # duration is total / K; the spread is that of the segment means.
+    nseg = max(1, min(20, args.steps))
+    bounds = [round(i * args.steps / nseg) for i in range(nseg + 1)]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(nseg + 1)]
     torch.cuda.synchronize()
-    t_begin.record(stream)
-    for i in range(args.steps):
-        q, k, v, S, Z, out = sets[i % N_SETS]
-        hba.step(q, k, v, W, S, Z, out=out)
-    t_end.record(stream)
+    marks[0].record(stream)
+    for sgi in range(nseg):
+        for i in range(bounds[sgi], bounds[sgi + 1]):
+            q, k, v, S, Z, out = sets[i % N_SETS]
+            hba.step(q, k, v, W, S, Z, out=out)
+        marks[sgi + 1].record(stream)
     torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
+    total_ms = marks[0].elapsed_time(marks[-1])
     ms_per_step = total_ms / args.steps
     mean_launch_ms = ms_per_step
+    seg_ms = [marks[i].elapsed_time(marks[i + 1]) / (bounds[i + 1] - bounds[i])
+              for i in range(nseg) if bounds[i + 1] > bounds[i]]
+    if len(seg_ms) >= 2:
+        dec = statistics.quantiles(seg_ms, n=10)
+        q10, q50, q90 = dec[0], statistics.median(seg_ms), dec[-1]
+    else:
+        q10 = q50 = q90 = ms_per_step
 
     nbytes = step_bytes(B, H, L, d, F)
     achieved = nbytes / (mean_launch_ms * 1e-3) / 1e9
@@ -371,8 +382,10 @@ def main():
                      "traffic": traffic,
                      "kernel": "hba_step (step_kernel<bf16,128,128>)",
                      "algorithmic_bytes_per_launch": nbytes,
-                     "launch_ms": {"mean": mean_launch_ms,
-                                   "timing": "K back-to-back launches between two HIP events on the launch stream"},
+                     "launch_ms": {"mean": mean_launch_ms, "p10": q10, "median": q50, "p90": q90,
+                                   "timing": (f"{args.steps} back-to-back launches on the launch stream, HIP "
+                                              f"events between {len(seg_ms)} segments; p10/median/p90 "
+                                              "of the segment means")},
                      "source_hash": khash},
         "cpu_baseline": base,
         "components": {"commit_block_us": commit_us,

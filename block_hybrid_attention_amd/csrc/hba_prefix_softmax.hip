@@ -7,13 +7,14 @@
 // prefix P, which is what the hybrid step's fixed-size state avoids.
 //
 // One workgroup (4 waves) per (request, head); the waves take interleaved
-// 16-key tiles and keep their own online-softmax state, merged in LDS at the
-// end.  Per tile:
-//   S^T = K Q^T on bf16 MFMA (fp32 MFMA for fp32 inputs): the accumulator
-//   layout gives each lane the scores of ONE query for four keys;
-//   O^T += V^T P^T on fp32 MFMA, whose B operand is exactly those four
-//   probabilities, so P never leaves registers and the per-query running max
-//   and sum live in the same lanes as the output rows they rescale.
+// key tiles and keep their own online-softmax state, merged in LDS at the
+// end.  The accumulator layout of S^T = K Q^T gives each lane the scores of
+// ONE query for a few keys, which is exactly the lane's share of P^T as an
+// MFMA operand of O^T += V^T P^T, so P never leaves registers and the running
+// max and sum of a query live in the lanes whose output rows they rescale.
+//   fp32 inputs: 16-key tiles, both products on fp32 MFMA.
+//   bf16 inputs: 32-key tiles, both products on bf16 MFMA (P split into a
+//   high part and a residual, V exact), V staged transposed in LDS.
 // The next tile's K and V are loaded before the current one is computed.
 #include "hba_device.h"
 #include "hba_internal.h"
@@ -244,9 +245,217 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(PrefixArgs a) {
     }
 }
 
+// bf16 inputs: both products on bf16 MFMA.  Waves take interleaved 32-key
+// tiles.  S^T = K Q^T as above (two 16-key halves), so a lane holds the
+// scores of one query for keys 4g..4g+3 and 16+4g..16+4g+3 (g = lane/16).
+// Those eight probabilities, in that order, are exactly the lane's B operand
+// of O^T += V^T P^T on v_mfma_f32_16x16x32_bf16, split into a bf16 high part
+// and a bf16 residual (V is exact in bf16), so P never leaves registers.  The
+// A operand needs eight keys of one V column per lane: each wave stages its
+// V tile transposed in its own LDS region (8x8 register transposes, keys in
+// the same order), read back as one 16-byte load per lane and column tile.
+template <int D>
+struct PrefixGeomBf16 {
+    static constexpr int VTLD = 4 * 8 + 8;                  // V^T row: 4 key groups x 8 keys + pad (bf16)
+    static constexpr int vt_bytes = D * VTLD * 2;           // one wave's V^T tile
+    static constexpr int OLD = D + 4;                       // merge row stride (floats)
+    static constexpr int ob_bytes = 4 * kRows * OLD * 4;    // the four waves' partial outputs
+    static constexpr int bytes = (4 * vt_bytes > ob_bytes ? 4 * vt_bytes : ob_bytes);
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void prefix_kernel_bf16(PrefixArgs a) {
+    using T = uint16_t;
+    using G = PrefixGeomBf16<D>;
+    constexpr int KS = D / 32;     // K-steps of S^T = K Q^T
+    constexpr int NCT = D / 16;    // 16-column output tiles
+    constexpr float kScaleLog2 = (D == 128 ? 0.08838834764831845f : 0.125f) * 1.4426950408889634f;
+    __shared__ __attribute__((aligned(16))) char smem[G::bytes];
+    __shared__ float mbuf[4][kRows], lbuf[4][kRows];
+
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int64_t bh = blockIdx.x;
+    const int b = (int)(bh / a.H);
+    const int L = a.L;
+    int P = a.prefix_len ? a.prefix_len[b] : a.P;
+    P = P < 0 ? 0 : (P > a.P ? a.P : P);
+    const int nkeys = P + L;
+    const int ntiles = (nkeys + 31) / 32;
+    T *vt = reinterpret_cast<T *>(smem + wave * G::vt_bytes);
+
+    // queries as the B operand of S^T = K Q^T: lane holds query 16 nt + li
+    const T *qg = static_cast<const T *>(a.q) + bh * L * D;
+    bf16x8 qq[2][KS];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int qi = 16 * nt + li;
+        const T *qr = qg + (int64_t)(qi < L ? qi : L - 1) * D + 8 * lg;
+#pragma unroll
+        for (int s_ = 0; s_ < KS; ++s_) qq[nt][s_] = *reinterpret_cast<const bf16x8 *>(qr + 32 * s_);
+    }
+
+    // one tile's operands: K rows j0 + 16 h + l%16 (A of S^T), and the V block
+    // of rows j0 + 4g + r, j0 + 16 + 4g + r (g = l/16, r < 4), columns 8 (l%16) ..
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    struct Tile {
+        u32x4 k[2][KS];
+        u32x4 v[8];
+    };
+    auto load = [&](int j0, Tile &t) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            int jk = j0 + 16 * hh + li;
+            jk = jk < nkeys ? jk : nkeys - 1;
+            const T *kr = key_row<T, D>(a, bh, P, jk) + 8 * lg;
+#pragma unroll
+            for (int s_ = 0; s_ < KS; ++s_) t.k[hh][s_] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kr + 32 * s_));
+        }
+        if (li < D / 8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                int jv = j0 + (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4);
+                jv = jv < nkeys ? jv : nkeys - 1;
+                const T *vr = val_row<T, D>(a, bh, P, jv) + 8 * li;
+                t.v[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vr));
+            }
+        }
+    };
+
+    floatx4 o[NCT][2];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) o[c][0] = o[c][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+
+    // one tile: V^T into the wave's LDS, scores, online softmax, O^T += V^T P^T
+    auto process = [&](int tile, const Tile &t) {
+        const int j0 = 32 * tile;
+            // V^T of this tile into the wave's LDS: row = column, 8 keys per group
+            if (li < D / 8) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                    uint32_t w[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        w[j] = __builtin_amdgcn_perm(t.v[2 * j + 1][c >> 1], t.v[2 * j][c >> 1], sel);
+                    *reinterpret_cast<uint4 *>(vt + (8 * li + c) * G::VTLD + 8 * lg) = make_uint4(w[0], w[1], w[2], w[3]);
+                }
+            }
+            // scores: s[hh][nt][r] = q_(16 nt + l%16) . k_(j0 + 16 hh + 4 (l/16) + r)
+            floatx4 sc[2][2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    sc[hh][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s_ = 0; s_ < KS; ++s_)
+                        sc[hh][nt] = mfma_bf16(__builtin_bit_cast(bf16x8, t.k[hh][s_]), qq[nt][s_], sc[hh][nt]);
+                }
+            bf16x8 ph[2], pl[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                float x[8];
+                float tmax = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int key = j0 + (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4);
+                    x[e] = key < nkeys ? sc[e >> 2][nt][e & 3] * kScaleLog2 : -INFINITY;
+                    tmax = fmaxf(tmax, x[e]);
+                }
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+                const float mnew = fmaxf(m[nt], tmax);   // finite: every tile has a valid key
+                const float corr = __builtin_amdgcn_exp2f(m[nt] - mnew);
+                float rs = 0.f, pv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    pv[e] = __builtin_amdgcn_exp2f(x[e] - mnew);
+                    rs += pv[e];
+                }
+                rs += __shfl_xor(rs, 16, kWave);
+                rs += __shfl_xor(rs, 32, kWave);
+                l[nt] = l[nt] * corr + rs;
+                m[nt] = mnew;
+#pragma unroll
+                for (int c = 0; c < NCT; ++c) o[c][nt] *= corr;
+                uint32_t hw[4], lw[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) split_pk_bf16(pv[2 * j], pv[2 * j + 1], hw[j], lw[j]);
+                ph[nt] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+                pl[nt] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+            }
+            // O^T += V^T P^T: o[c][nt][r] = O[16 nt + l%16][16 c + 4 (l/16) + r]
+#pragma unroll
+            for (int c = 0; c < NCT; ++c) {
+                const bf16x8 va = *reinterpret_cast<const bf16x8 *>(vt + (16 * c + li) * G::VTLD + 8 * lg);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    o[c][nt] = mfma_bf16(va, ph[nt], o[c][nt]);
+                    o[c][nt] = mfma_bf16(va, pl[nt], o[c][nt]);
+                }
+            }
+    };
+    // two tiles in flight per wave, ping-ponged without copies (a register
+    // copy of the prefetched tile would wait for all of its loads)
+    Tile t0, t1;
+    if (wave < ntiles) load(32 * wave, t0);
+#pragma unroll 1
+    for (int tile = wave; tile < ntiles; tile += 8) {
+        load(32 * (tile + 4 < ntiles ? tile + 4 : ntiles - 1), t1);
+        process(tile, t0);
+        if (tile + 4 >= ntiles) break;
+        load(32 * (tile + 8 < ntiles ? tile + 8 : ntiles - 1), t0);
+        process(tile + 4, t1);
+    }
+
+    // merge the four waves' partial softmax states (the V^T tiles are dead)
+    if (lg == 0) {
+        mbuf[wave][li] = m[0];
+        mbuf[wave][16 + li] = m[1];
+        lbuf[wave][li] = l[0];
+        lbuf[wave][16 + li] = l[1];
+    }
+    __syncthreads();
+    float *obuf = reinterpret_cast<float *>(smem);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int qi = 16 * nt + li;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, mbuf[w][qi]);
+        float Lt = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) Lt += lbuf[w][qi] * __builtin_amdgcn_exp2f(mbuf[w][qi] - M);
+        const float sc_ = __builtin_amdgcn_exp2f(m[nt] - M) / Lt;
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+            *reinterpret_cast<float4 *>(obuf + (wave * kRows + qi) * G::OLD + 16 * c + 4 * lg) =
+                make_float4(o[c][nt][0] * sc_, o[c][nt][1] * sc_, o[c][nt][2] * sc_, o[c][nt][3] * sc_);
+    }
+    __syncthreads();
+    float *og = a.out + bh * L * D;
+#pragma unroll
+    for (int it = 0; it < kRows * D / 4 / kThreads; ++it) {
+        const int e = tid + it * kThreads;
+        const int qi = e / (D / 4), c = 4 * (e % (D / 4));
+        if (qi < L) {
+            floatx4 v = *reinterpret_cast<const floatx4 *>(obuf + (0 * kRows + qi) * G::OLD + c);
+#pragma unroll
+            for (int w = 1; w < 4; ++w) v += *reinterpret_cast<const floatx4 *>(obuf + (w * kRows + qi) * G::OLD + c);
+            __builtin_nontemporal_store(v, reinterpret_cast<floatx4 *>(og + (int64_t)qi * D + c));
+        }
+    }
+}
+
 template <typename T, int D>
 static hipError_t launch_prefix_t(const PrefixArgs &a, hipStream_t stream) {
-    return launch_kernel(prefix_kernel<T, D>, dim3((unsigned)(a.B * a.H)), dim3(kThreads), a, stream);
+    if constexpr (sizeof(T) == 2)
+        return launch_kernel(prefix_kernel_bf16<D>, dim3((unsigned)(a.B * a.H)), dim3(kThreads), a, stream);
+    else
+        return launch_kernel(prefix_kernel<T, D>, dim3((unsigned)(a.B * a.H)), dim3(kThreads), a, stream);
 }
 
 hipError_t launch_prefix_softmax(const PrefixArgs &a, bool bf16, int d, hipStream_t stream) {
