@@ -252,35 +252,36 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
 
     // staging of one chunk: W blocks (when needed), v blocks and the k tile
     auto stage = [&](int t0, int nrows, bool with_w) {
-        uint4 wb[8], vb[8], kb[KCH / kThreads];
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 wb[8], vb[8], kb[KCH / kThreads];
         const bool do_w = with_w && tid < WBLK;
         const bool do_v = tid < VBLK;
         if (do_w) {
             const int bf = tid % (F / 8), bi = tid / (F / 8);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) wb[e] = *reinterpret_cast<const uint4 *>(Wg + (int64_t)(8 * bi + e) * F + 8 * bf);
+            for (int e = 0; e < 8; ++e) wb[e] = *reinterpret_cast<const u32x4 *>(Wg + (int64_t)(8 * bi + e) * F + 8 * bf);
         }
         if (do_v) {
             const int bc = tid % (D / 8), bt = tid / (D / 8);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int t = 8 * bt + e;
-                const uint4 x = *reinterpret_cast<const uint4 *>(vg + (int64_t)(t0 + (t < nrows ? t : nrows - 1)) * D + 8 * bc);
-                vb[e] = t < nrows ? x : make_uint4(0u, 0u, 0u, 0u);
+                const u32x4 x = *reinterpret_cast<const u32x4 *>(vg + (int64_t)(t0 + (t < nrows ? t : nrows - 1)) * D + 8 * bc);
+                vb[e] = t < nrows ? x : u32x4{0u, 0u, 0u, 0u};
             }
         }
 #pragma unroll
         for (int it = 0; it < KCH / kThreads; ++it) {
             const int c = tid + it * kThreads;
             const int kr = c / (D / 8), kc = (c % (D / 8)) * 8;
-            const uint4 x = *reinterpret_cast<const uint4 *>(kg + (int64_t)(t0 + (kr < nrows ? kr : nrows - 1)) * D + kc);
-            kb[it] = kr < nrows ? x : make_uint4(0u, 0u, 0u, 0u);
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(kg + (int64_t)(t0 + (kr < nrows ? kr : nrows - 1)) * D + kc);
+            kb[it] = kr < nrows ? x : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int it = 0; it < KCH / kThreads; ++it) {
             const int c = tid + it * kThreads;
             const int kr = c / (D / 8), kc = (c % (D / 8)) * 8;
-            *reinterpret_cast<uint4 *>(ks + kr * P::XLD + kc) = kb[it];
+            *reinterpret_cast<u32x4 *>(ks + kr * P::XLD + kc) = kb[it];
         }
         // 8x8 transposes in registers: output row c of a block = its column c
         if (do_w) {
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
                 uint32_t w[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    w[j] = __builtin_amdgcn_perm(u4_word(wb[2 * j + 1], c >> 1), u4_word(wb[2 * j], c >> 1), sel);
+                    w[j] = __builtin_amdgcn_perm(wb[2 * j + 1][c >> 1], wb[2 * j][c >> 1], sel);
                 *reinterpret_cast<uint4 *>(ws + (8 * bf + c) * P::WLD + 8 * bi) = make_uint4(w[0], w[1], w[2], w[3]);
             }
         }
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
                 uint32_t w[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    w[j] = __builtin_amdgcn_perm(u4_word(vb[2 * j + 1], c >> 1), u4_word(vb[2 * j], c >> 1), sel);
+                    w[j] = __builtin_amdgcn_perm(vb[2 * j + 1][c >> 1], vb[2 * j][c >> 1], sel);
                 *reinterpret_cast<uint4 *>(vt + rho * G::TP + 8 * bt) = make_uint4(w[0], w[1], w[2], w[3]);
             }
         }
@@ -324,11 +325,11 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
                 const float *p = Sg + (int64_t)(f_base + 16 * mt + 4 * lg + r) * D + NE * li;
 #pragma unroll
                 for (int q = 0; q < NE / 4; ++q) {
-                    const float4 t = reinterpret_cast<const float4 *>(p)[q];
-                    acc[mt][4 * q + 0][r] = t.x;
-                    acc[mt][4 * q + 1][r] = t.y;
-                    acc[mt][4 * q + 2][r] = t.z;
-                    acc[mt][4 * q + 3][r] = t.w;
+                    const floatx4 t = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p) + q);
+                    acc[mt][4 * q + 0][r] = t[0];
+                    acc[mt][4 * q + 1][r] = t[1];
+                    acc[mt][4 * q + 2][r] = t[2];
+                    acc[mt][4 * q + 3][r] = t[3];
                 }
             }
     };
@@ -409,10 +410,11 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
             float *p = Sg + (int64_t)(f_base + 16 * mt + 4 * lg + r) * D + NE * li;
 #pragma unroll
             for (int q = 0; q < NE / 4; ++q)
-                reinterpret_cast<float4 *>(p)[q] = make_float4(acc[mt][4 * q + 0][r], acc[mt][4 * q + 1][r],
-                                                                acc[mt][4 * q + 2][r], acc[mt][4 * q + 3][r]);
+                __builtin_nontemporal_store(floatx4{acc[mt][4 * q + 0][r], acc[mt][4 * q + 1][r],
+                                                    acc[mt][4 * q + 2][r], acc[mt][4 * q + 3][r]},
+                                            reinterpret_cast<floatx4 *>(p) + q);
         }
-    if (zf >= 0 && zf < F) Zg[zf] = zacc;
+    if (zf >= 0 && zf < F) __builtin_nontemporal_store(zacc, Zg + zf);
 }
 
 template <typename T, int D, int F>
