@@ -353,6 +353,14 @@ def main():
     cbytes = commit_bytes(B, H, L, d, F)
     del Sc, Zc
 
+    # the standalone feature map (hba_feature_map) of the step's B*L query
+    # rows for all heads: x [B*L][H][d] bf16 -> phi [B*L][H][2F] fp32
+    xq = q.permute(0, 2, 1, 3).reshape(B * L, H, d).contiguous()
+    phi = torch.empty((B * L, H, 2 * F), device=dev)
+    fm_ms = _time_launches(torch, lambda: hba.feature_map(xq, W, out=phi), 3, 20, stream)
+    fm_bytes = B * L * H * d * 2 + H * d * F * 2 + B * L * H * 2 * F * 4
+    del xq, phi
+
     base = None
     if not args.no_cpu_baseline:
         q0, k0, v0 = sets[0][0], sets[0][1], sets[0][2]
@@ -390,7 +398,10 @@ def main():
         "cpu_baseline": base,
         "components": {"commit_block_us": commit_us,
                        "commit_block_GBps": cbytes / (commit_us * 1e-6) / 1e9,
-                       "commit_algorithmic_bytes": cbytes},
+                       "commit_algorithmic_bytes": cbytes,
+                       "feature_map_us": fm_ms * 1e3,
+                       "feature_map_GBps": fm_bytes / (fm_ms * 1e-3) / 1e9,
+                       "feature_map_algorithmic_bytes": fm_bytes},
     }
     print(json.dumps(line), flush=True)
 
