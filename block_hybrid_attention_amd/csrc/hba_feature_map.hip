@@ -3,11 +3,10 @@
 // "Retrofitting Linear Attention into Diffusion Language Models", section 3.1:
 //   phi(x) = [softmax(x W), softmax(-x W)] in R^{2F}, W in R^{d x F} per head.
 //
-// One workgroup per (32-row tile, head): the x rows and W go through LDS,
-// u = x W runs on MFMA (bf16 or fp32), and each wave turns 8 rows of u into
-// phi with wave-wide max/min/sum reductions, writing 2F contiguous fp32 per
-// row.  The same device code forms phi(q) inside the step and phi(k) inside
-// the commit.
+// fp32 inputs: one workgroup per (32-row tile, head): the x rows and W go
+// through LDS, u = x W runs on fp32 MFMA, and each wave turns 8 rows of u
+// into phi with wave-wide max/min/sum reductions, writing 2F contiguous fp32
+// per row (the same device code forms phi(k) in the fp32 commit).
 #include "hba_device.h"
 #include "hba_internal.h"
 
@@ -52,10 +51,134 @@ __global__ __launch_bounds__(kThreads) void feature_map_kernel(FeatureMapArgs a)
     }
 }
 
+// bf16 inputs: one workgroup per (4 row tiles of 32, head), W^T staged in LDS
+// once.  Per tile, u^T = W^T x^T runs on bf16 MFMA with the x rows loaded
+// straight into the B operand layout (lane: row 16 g + l%16, 8 values of d
+// at 32 s + 8 (l/16)), so a lane holds F/4 features of ONE row and its softmax
+// reductions are in registers plus two cross-lane steps.  Waves 0-1 form the
+// softmax(u) half of rows 0-15 / 16-31, waves 2-3 the softmax(-u) half.  The
+// tile of phi goes through LDS so each row (2F floats) is written by whole
+// lanes of a wave with 16-byte nontemporal stores.  The next tile's x is
+// requested before the current tile is computed.
+template <int D, int F>
+struct FmGeomBf16 {
+    using P = ProjGeom<uint16_t, D, F>;
+    static constexpr int PLD = 2 * F + 4;            // phi tile row stride (floats)
+    static constexpr int phi_off = P::w_bytes;
+    static constexpr int bytes = P::w_bytes + kRows * PLD * 4;
+};
+constexpr int kFmTiles = 4;   // 32-row tiles per workgroup
+
+template <int D, int F>
+__global__ __launch_bounds__(kThreads, 2) void feature_map_kernel_bf16(FeatureMapArgs a) {
+    using T = uint16_t;
+    using P = ProjGeom<T, D, F>;
+    using G = FmGeomBf16<D, F>;
+    constexpr int KS = D / 32;      // K-steps of the projection
+    constexpr int NT = F / 16;      // 16-feature tiles of u^T
+    constexpr int RV = 2 * F / 4;   // float4 per phi row
+    __shared__ __attribute__((aligned(16))) char smem[G::bytes];
+    T *ws = reinterpret_cast<T *>(smem);
+    float *ph = reinterpret_cast<float *>(smem + G::phi_off);
+
+    const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int qgrp = wave & 1, half = wave >> 1;
+    const int h = (int)blockIdx.y;
+    const int64_t n = a.n;
+    const int64_t tile0 = (int64_t)blockIdx.x * kFmTiles;
+    const T *xg = static_cast<const T *>(a.x);
+
+    auto load_x = [&](int64_t r0, bf16x8 (&xo)[KS]) {
+        int64_t row = r0 + 16 * qgrp + li;
+        row = row < n ? row : n - 1;   // rows past the end repeat the last one (not stored)
+        const T *p = xg + (row * a.H + h) * D + 8 * lg;
+#pragma unroll
+        for (int s_ = 0; s_ < KS; ++s_) xo[s_] = *reinterpret_cast<const bf16x8 *>(p + 32 * s_);
+    };
+    bf16x8 xo[2][KS];
+    load_x(tile0 * kRows, xo[0]);
+    {
+        WChunks<T, D, F> wc;
+        load_w<T, D, F>(static_cast<const T *>(a.W) + (int64_t)h * D * F, wc);
+        store_w<T, D, F>(wc, ws);
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int t = 0; t < kFmTiles; ++t) {
+        const int64_t r0 = (tile0 + t) * kRows;
+        if (r0 >= n) break;   // uniform over the workgroup
+        if (t + 1 < kFmTiles) {
+            const int64_t rn = r0 + kRows;
+            load_x(rn < n ? rn : r0, xo[(t + 1) & 1]);
+        }
+        // u^T: acc[m][r] = u[row 16 qgrp + l%16][feature 16m + 4(l/16) + r]
+        floatx4 acc[NT];
+#pragma unroll
+        for (int m = 0; m < NT; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s_ = 0; s_ < KS; ++s_)
+#pragma unroll
+            for (int m = 0; m < NT; ++m) {
+                const bf16x8 aw = *reinterpret_cast<const bf16x8 *>(ws + (16 * m + li) * P::WLD + 32 * s_ + 8 * lg);
+                acc[m] = mfma_bf16(aw, xo[t & 1][s_], acc[m]);
+            }
+        // this wave's half: softmax over the F features of sgn * u
+        const float sgn2 = half ? -kLog2e : kLog2e;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int m = 0; m < NT; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                acc[m][r] *= sgn2;
+                mx = fmaxf(mx, acc[m][r]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        float sm = 0.f;
+#pragma unroll
+        for (int m = 0; m < NT; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                acc[m][r] = fast_exp2(acc[m][r] - mx);
+                sm += acc[m][r];
+            }
+        sm += __shfl_xor(sm, 16, kWave);
+        sm += __shfl_xor(sm, 32, kWave);
+        const float is = 1.0f / sm;
+        float *prow = ph + (16 * qgrp + li) * G::PLD + half * F + 4 * lg;
+#pragma unroll
+        for (int m = 0; m < NT; ++m)
+            *reinterpret_cast<float4 *>(prow + 16 * m) =
+                make_float4(acc[m][0] * is, acc[m][1] * is, acc[m][2] * is, acc[m][3] * is);
+        __syncthreads();
+        // store the tile row by row: 2F contiguous floats per (row, head)
+        const int nrows = n - r0 < kRows ? (int)(n - r0) : kRows;
+#pragma unroll
+        for (int ii = 0; ii < kRows / 4; ++ii) {
+            const int i = 4 * ii + wave;
+            if (i < nrows) {
+                float *o = a.phi + ((r0 + i) * a.H + h) * (2 * F);
+#pragma unroll
+                for (int e = lane; e < RV; e += kWave)
+                    __builtin_nontemporal_store(*reinterpret_cast<const floatx4 *>(ph + i * G::PLD + 4 * e),
+                                                reinterpret_cast<floatx4 *>(o) + e);
+            }
+        }
+        __syncthreads();   // the phi tile is rewritten by the next tile
+    }
+}
+
 template <typename T, int D, int F>
 static hipError_t launch_fm_t(const FeatureMapArgs &a, hipStream_t stream) {
-    const unsigned tiles = (unsigned)((a.n + kRows - 1) / kRows);
-    return launch_kernel(feature_map_kernel<T, D, F>, dim3(tiles, (unsigned)a.H), dim3(kThreads), a, stream);
+    const int64_t tiles = (a.n + kRows - 1) / kRows;
+    if constexpr (sizeof(T) == 2) {
+        const unsigned groups = (unsigned)((tiles + kFmTiles - 1) / kFmTiles);
+        return launch_kernel(feature_map_kernel_bf16<D, F>, dim3(groups, (unsigned)a.H), dim3(kThreads), a, stream);
+    } else {
+        return launch_kernel(feature_map_kernel<T, D, F>, dim3((unsigned)tiles, (unsigned)a.H), dim3(kThreads), a, stream);
+    }
 }
 
 hipError_t launch_feature_map(const FeatureMapArgs &a, bool bf16, int d, int F, hipStream_t stream) {

@@ -55,6 +55,19 @@ def test_feature_map(dtype, d, F):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("d,F", [(128, 128), (64, 128)])
+def test_feature_map_many_tiles(d, F):
+    """Several workgroups of four 32-row tiles each, and a ragged last tile."""
+    g = gen(170 + d + F)
+    H, n = 3, 300
+    x = wl.normal((n, H, d), 1.0, torch.bfloat16, g, DEV)
+    W = wl.feature_weights(H, d, F, torch.bfloat16, g, DEV)
+    phi = hba.feature_map(x, W)
+    err = row_rel(phi, oracle.feature_map(x, W))
+    report(f"feature_map bf16 n={n} d={d} F={F}", phi=err)
+    assert err <= TOL[torch.bfloat16]
+
+
 # ---------------------------------------------------- tiny fp32 workload
 def test_tiny_fp32_workload():
     """1 request, 1 head, d = F = 64, 4 committed 8-token blocks, then a step."""
