@@ -170,6 +170,13 @@ def decode_loop(args, torch, hba, wl, dev):
             hba.step(q, k, v, W, S, Z, out=out)
         hba.commit(k, v, W, S, Z)
 
+    def block_fused(n):   # the last step and the commit as one call
+        for s_ in range(nsteps - 1):
+            q, k, v = pool[(n * nsteps + s_) % len(pool)]
+            hba.step(q, k, v, W, S, Z, out=out)
+        q, k, v = pool[(n * nsteps + nsteps - 1) % len(pool)]
+        hba.step_commit(q, k, v, W, S, Z, out=out)
+
     for n in range(2):
         block(n)
     S.zero_()
@@ -182,9 +189,24 @@ def decode_loop(args, torch, hba, wl, dev):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
+
+    # the same loop with the last step of each block fused with its commit
+    S.zero_()
+    Z.zero_()
+    for n in range(2):
+        block_fused(n)
+    S.zero_()
+    Z.zero_()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for n in range(args.blocks):
+        block_fused(n)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_f = e0.elapsed_time(e1)
     final_eager = (S.clone(), Z.clone(), out.clone())
 
-    # The same loop replayed from a HIP graph of two blocks (the input pool
+    # the fused loop replayed from a HIP graph of two blocks (the input pool
     # repeats every two blocks), starting from the same zero state.  The
     # state is cleared outside the graph.  Replays are checked against the
     # eager loop after 2 and 4 blocks (with eager work and synchronisation
@@ -193,7 +215,7 @@ def decode_loop(args, torch, hba, wl, dev):
         S.zero_()
         Z.zero_()
         for n in range(nblocks):
-            block(n)
+            block_fused(n)
         torch.cuda.synchronize()
         return S.clone(), Z.clone(), out.clone()
 
@@ -203,8 +225,8 @@ def decode_loop(args, torch, hba, wl, dev):
     ref2, ref4 = eager_from_zero(2), eager_from_zero(4)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        block(0)
-        block(1)
+        block_fused(0)
+        block_fused(1)
     S.zero_()
     Z.zero_()
     graph.replay()
@@ -229,9 +251,11 @@ def decode_loop(args, torch, hba, wl, dev):
                       "blocks": args.blocks, "total_ms": ms, "us_per_block": ms * 1e3 / args.blocks,
                       "generated_tokens_per_s": B * L * args.blocks / (ms * 1e-3),
                       "query_tokens_per_s": B * L * nsteps * args.blocks / (ms * 1e-3),
-                      "graph": {"blocks": 2 * reps, "us_per_block": ms_g * 1e3 / (2 * reps),
-                                "generated_tokens_per_s": B * L * 2 * reps / (ms_g * 1e-3),
-                                "matches_eager": ok}}), flush=True)
+                      "fused_last_step": {"us_per_block": ms_f * 1e3 / args.blocks,
+                                          "generated_tokens_per_s": B * L * args.blocks / (ms_f * 1e-3)},
+                      "fused_graph": {"blocks": 2 * reps, "us_per_block": ms_g * 1e3 / (2 * reps),
+                                      "generated_tokens_per_s": B * L * 2 * reps / (ms_g * 1e-3),
+                                      "matches_eager": ok}}), flush=True)
 
 
 def main():
@@ -353,6 +377,13 @@ def main():
     cbytes = commit_bytes(B, H, L, d, F)
     del Sc, Zc
 
+    # the fused last step + commit (hba_step_commit) at the same shape, on a copy
+    Sf, Zf = S.clone(), Z.clone()
+    outf = torch.empty_like(out)
+    sc_ms = _time_launches(torch, lambda: hba.step_commit(q, k, v, W, Sf, Zf, out=outf), 3, 20, stream)
+    sc_bytes = step_bytes(B, H, L, d, F) + B * H * 2 * F * (d + 1) * 4
+    del Sf, Zf, outf
+
     # the standalone feature map (hba_feature_map) of the step's B*L query
     # rows for all heads: x [B*L][H][d] bf16 -> phi [B*L][H][2F] fp32
     xq = q.permute(0, 2, 1, 3).reshape(B * L, H, d).contiguous()
@@ -399,6 +430,9 @@ def main():
         "components": {"commit_block_us": commit_us,
                        "commit_block_GBps": cbytes / (commit_us * 1e-6) / 1e9,
                        "commit_algorithmic_bytes": cbytes,
+                       "step_commit_us": sc_ms * 1e3,
+                       "step_commit_GBps": sc_bytes / (sc_ms * 1e-3) / 1e9,
+                       "step_commit_algorithmic_bytes": sc_bytes,
                        "feature_map_us": fm_ms * 1e3,
                        "feature_map_GBps": fm_bytes / (fm_ms * 1e-3) / 1e9,
                        "feature_map_algorithmic_bytes": fm_bytes},

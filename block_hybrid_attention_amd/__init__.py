@@ -22,7 +22,7 @@ import torch
 from .pool import StatePool  # noqa: F401  (re-exported)
 
 __all__ = ["feature_map", "step", "commit", "prefix_softmax", "StatePool", "HbaError",
-           "library_path", "load_library", "abi_version"]
+           "library_path", "load_library", "abi_version", "step_commit"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libhba.so")
@@ -70,7 +70,9 @@ def load_library():
         lib.hba_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.hba_commit.argtypes = [sp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.hba_prefix_softmax.argtypes = [sp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp]
-        for fn in (lib.hba_feature_map, lib.hba_step, lib.hba_commit, lib.hba_prefix_softmax):
+        lib.hba_step_commit.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        for fn in (lib.hba_feature_map, lib.hba_step, lib.hba_commit, lib.hba_prefix_softmax,
+                   lib.hba_step_commit):
             fn.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -175,6 +177,34 @@ def step(q, k, v, W, S_pool, Z_pool, gate=None, slot=None, out=None, stream=None
     shape = Shape(B, H, L, d, F, dt, n_slots)
     _call(lib.hba_step, "hba_step", ctypes.byref(shape), _p(q), _p(k), _p(v), _p(W), _p(gate),
           _p(S_pool), _p(Z_pool), _p(slot), _p(out), _stream(stream))
+    return out
+
+
+def step_commit(q, k, v, W, S_pool, Z_pool, gate=None, slot=None, n_valid=None, out=None, stream=None):
+    """The block's last denoising step fused with its commit (sections 3.1, 3.3):
+    out = step(q, k, v) on the states as they are, then S += sum_t phi(k_t) v_t^T,
+    Z += sum_t phi(k_t) over the first n_valid[b] tokens (all L when None).
+    Shapes as for step(); S_pool and Z_pool are updated in place."""
+    lib = load_library()
+    B, H, L, d = q.shape
+    F = W.shape[2]
+    dt = _in_dtype(q, k, v, W)
+    for t, nm in ((k, "k"), (v, "v")):
+        _check(t, (B, H, L, d), q.dtype, nm)
+    _check(W, (H, d, F), q.dtype, "W")
+    n_slots = S_pool.shape[0]
+    _check(S_pool, (n_slots, H, 2 * F, d), torch.float32, "S_pool")
+    _check(Z_pool, (n_slots, H, 2 * F), torch.float32, "Z_pool")
+    _check(gate, (H,), torch.float32, "gate")
+    _check(slot, (B,), torch.int32, "slot")
+    _check(n_valid, (B,), torch.int32, "n_valid")
+    if out is None:
+        out = torch.empty((B, H, L, d), device=q.device, dtype=torch.float32)
+    _check(out, (B, H, L, d), torch.float32, "out")
+    _dev(q, k, v, W, S_pool, Z_pool, gate, slot, n_valid, out)
+    shape = Shape(B, H, L, d, F, dt, n_slots)
+    _call(lib.hba_step_commit, "hba_step_commit", ctypes.byref(shape), _p(n_valid), _p(q), _p(k), _p(v),
+          _p(W), _p(gate), _p(S_pool), _p(Z_pool), _p(slot), _p(out), _stream(stream))
     return out
 
 

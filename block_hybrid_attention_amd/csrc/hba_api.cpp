@@ -48,7 +48,7 @@ const char *hba_status_string(hba_status st) {
     return "unknown status";
 }
 
-int32_t hba_abi_version(void) { return 1; }
+int32_t hba_abi_version(void) { return 2; }
 
 hba_status hba_feature_map(const hba_shape *shape, int64_t n_rows, const void *x, const void *W,
                            float *phi, void *stream) {
@@ -96,6 +96,25 @@ hba_status hba_commit(const hba_shape *shape, int32_t n_tok, const int32_t *n_va
     hba::CommitArgs a{n_valid, k, v, W, S_pool, Z_pool, slot, shape->batch, shape->heads, n_tok};
     return from_hip(hba::launch_commit(a, shape->in_dtype == HBA_BF16, shape->head_dim, shape->feat,
                                        static_cast<hipStream_t>(stream)));
+}
+
+hba_status hba_step_commit(const hba_shape *shape, const int32_t *n_valid, const void *q, const void *k,
+                           const void *v, const void *W, const float *gate, float *S_pool, float *Z_pool,
+                           const int32_t *slot, float *out, void *stream) {
+    hba_status st = check_common(shape, true, true);
+    if (st != HBA_OK) return st;
+    if (shape->n_slots < 0) return HBA_ERR_SHAPE;
+    if (shape->batch == 0) return HBA_OK;
+    if (!q || !k || !v || !W || !S_pool || !Z_pool || !out) return HBA_ERR_NULL;
+    if (!slot && shape->batch > shape->n_slots) return HBA_ERR_CAPACITY;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(W) || !aligned16(S_pool) ||
+        !aligned16(Z_pool) || !aligned16(out) || (gate && !aligned4(gate)) || (slot && !aligned4(slot)) ||
+        (n_valid && !aligned4(n_valid)))
+        return HBA_ERR_ALIGN;
+    hba::StepCommitArgs a{q, k, v, W, gate, S_pool, Z_pool, slot, n_valid, out, shape->batch, shape->heads,
+                          shape->block};
+    return from_hip(hba::launch_step_commit(a, shape->in_dtype == HBA_BF16, shape->head_dim, shape->feat,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 hba_status hba_prefix_softmax(const hba_shape *shape, int32_t max_prefix, const int32_t *prefix_len,

@@ -36,6 +36,10 @@ __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_bits_to_f32(x)
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){a, b}, bf16x2));
 }
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): the residual as a float
+__device__ __forceinline__ float bf16_residual(float x) {
+    return x - (float)(__bf16)x;
+}
 // Split two floats into packed bf16 high parts and packed bf16 residuals:
 // x = hi + lo + O(2^-17 |x|).
 __device__ __forceinline__ void split_pk_bf16(float a, float b, uint32_t &hi, uint32_t &lo) {

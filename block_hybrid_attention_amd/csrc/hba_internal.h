@@ -27,6 +27,17 @@ struct StepArgs {
     int B, H, L;
 };
 
+struct StepCommitArgs {
+    const void *q, *k, *v;   // [B][H][L][d]
+    const void *W;           // [H][d][F]
+    const float *gate;       // [H] or null
+    float *S;                // [slots][H][2F][d], updated in place
+    float *Z;                // [slots][H][2F], updated in place
+    const int32_t *slot;     // [B] or null
+    const int32_t *n_valid;  // [B] or null
+    float *out;              // [B][H][L][d]
+    int B, H, L;
+};
 struct CommitArgs {
     const int32_t *n_valid;  // [B] or null
     const void *k, *v;       // [B][H][T][d]
@@ -60,6 +71,7 @@ hipError_t launch_feature_map(const FeatureMapArgs &a, bool dtype_bf16, int d, i
                               hipStream_t stream);
 hipError_t launch_step(const StepArgs &a, bool dtype_bf16, int d, int F, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &a, bool dtype_bf16, int d, int F, hipStream_t stream);
+hipError_t launch_step_commit(const StepCommitArgs &a, bool dtype_bf16, int d, int F, hipStream_t stream);
 hipError_t launch_prefix_softmax(const PrefixArgs &a, bool dtype_bf16, int d, hipStream_t stream);
 
 }  // namespace hba

@@ -386,10 +386,6 @@ struct StepGeomBf16 {
     static constexpr int bytes = row_off + 3 * kRows * 4;
 };
 
-// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi)
-__device__ __forceinline__ float bf16_residual(float x) {
-    return x - (float)(__bf16)x;
-}
 
 template <int D, int F, int NSPLIT>
 __global__ __launch_bounds__(kThreads, 3) void step_kernel_bf16(StepArgs a) {

@@ -128,6 +128,27 @@ hba_status hba_commit(const hba_shape *shape, int32_t n_tok, const int32_t *n_va
                       const void *k, const void *v, const void *W, float *S_pool,
                       float *Z_pool, const int32_t *slot, void *stream);
 
+/* The last denoising step of a block fused with the commit of that block
+ * (section 3.1; section 3.3 describes one launch per hybrid layer with its
+ * causal state update).  Equivalent to hba_step(...) on the state as it is,
+ * followed by hba_commit(n_tok = block, n_valid, k, v, ...): out is computed
+ * from the old S and Z, then
+ *   S += sum_t phi(k_t) v_t^T,   Z += sum_t phi(k_t)   (t < n_valid[b])
+ * with the block's own keys and values.  For bf16 inputs with head_dim 128
+ * it is one kernel that reads S once and writes it once; other shapes run
+ * the step kernel and then the commit kernel.
+ * Reads: batch, heads, block, head_dim, feat, in_dtype, n_slots.
+ *   n_valid  [B] int32 or NULL   tokens of the block to fold; NULL means the
+ *                                whole block.  Precondition: 0 <= n_valid[b] <= block.
+ *   q, k, v, W, gate, slot, out  as for hba_step
+ *   S_pool, Z_pool               as for hba_commit, updated in place.
+ *                                Precondition: slots distinct within one call.
+ * Errors: as for hba_step and hba_commit; nothing is launched on an error. */
+hba_status hba_step_commit(const hba_shape *shape, const int32_t *n_valid, const void *q,
+                           const void *k, const void *v, const void *W, const float *gate,
+                           float *S_pool, float *Z_pool, const int32_t *slot, float *out,
+                           void *stream);
+
 /* Comparator: full softmax attention (section 2.2) of the active block's
  * queries over the request's cached prefix followed by the block itself,
  * scale 1/sqrt(d), every key visible, no gate -- the prefix attention that
@@ -148,7 +169,7 @@ hba_status hba_prefix_softmax(const hba_shape *shape, int32_t max_prefix,
 /* Static description of a status code (never NULL). */
 const char *hba_status_string(hba_status status);
 
-/* Library ABI version, currently 1. */
+/* Library ABI version, currently 2 (2 added hba_step_commit). */
 int32_t hba_abi_version(void);
 
 #ifdef __cplusplus

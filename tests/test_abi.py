@@ -36,12 +36,12 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"hba_feature_map", "hba_step", "hba_commit", "hba_prefix_softmax",
+    assert {"hba_feature_map", "hba_step", "hba_commit", "hba_prefix_softmax", "hba_step_commit",
             "hba_status_string", "hba_abi_version"} <= set(names)
     L = lib()
     for n in names:
         assert hasattr(L, n), n
-    assert hba.abi_version() == 1
+    assert hba.abi_version() == 2
 
 
 def test_status_strings():
@@ -92,6 +92,27 @@ def test_zero_batch_is_a_noop():
     assert L.hba_commit(ctypes.byref(sh), 32, None, None, None, None, None, None, None, None) == OK
     assert L.hba_prefix_softmax(ctypes.byref(sh), 64, None, None, None, None, None, None, None, None) == OK
     assert L.hba_feature_map(ctypes.byref(shape()), 0, None, None, None, None) == OK
+
+
+@no_gpu_only
+def test_step_commit_validation():
+    L = lib()
+
+    def call(sh, q=A, k=A, v=A, W=A, gate=None, S=A2, Z=A2, slot=None, out=A2, n_valid=None):
+        return L.hba_step_commit(ctypes.byref(sh) if sh is not None else None, n_valid, q, k, v, W, gate,
+                                 S, Z, slot, out, None)
+
+    assert call(None) == ENULL
+    assert call(shape(dtype=3)) == EDTYPE
+    assert call(shape(d=96)) == EUNSUP
+    assert call(shape(block=0)) == ESHAPE
+    assert call(shape(block=40)) == EUNSUP
+    assert call(shape(), v=None) == ENULL
+    assert call(shape(), Z=None) == ENULL
+    assert call(shape(batch=9, slots=8)) == ECAP
+    assert call(shape(), S=MIS) == EALIGN
+    assert call(shape(), n_valid=ctypes.c_void_p(0x10002), slot=A) == EALIGN
+    assert call(shape(batch=0), q=None, k=None, v=None, W=None, S=None, Z=None, out=None) == OK
 
 
 @no_gpu_only
