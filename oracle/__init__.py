@@ -54,11 +54,11 @@ def _lib():
         lib.orc_threads.argtypes = [ctypes.c_int]
         lib.orc_threads.restype = ctypes.c_int
         lib.orc_feature_map.argtypes = [i64, i32, i32, i32, _f64p, _f64p, _f64p, ctypes.c_int]
-        lib.orc_commit.argtypes = [i32, i32, i32, i32, i32, _i32p, _f64p, _f64p, _f64p,
+        lib.orc_commit.argtypes = [i32, i32, i32, i32, i32, i32, _i32p, _f64p, _f64p, _f64p,
                                    _f64p, _f64p, _i32p, ctypes.c_int]
-        lib.orc_step.argtypes = [i32, i32, i32, i32, i32, _f64p, _f64p, _f64p, _f64p, _f64p,
+        lib.orc_step.argtypes = [i32, i32, i32, i32, i32, i32, _f64p, _f64p, _f64p, _f64p, _f64p,
                                  _f64p, _f64p, _i32p, _f64p, ctypes.c_int]
-        lib.orc_prefix_softmax.argtypes = [i32, i32, i32, i32, i32, _i32p, _f64p, _f64p, _f64p,
+        lib.orc_prefix_softmax.argtypes = [i32, i32, i32, i32, i32, i32, _i32p, _f64p, _f64p, _f64p,
                                            _f64p, _f64p, _f64p, ctypes.c_int]
         for fn in (lib.orc_feature_map, lib.orc_commit, lib.orc_step, lib.orc_prefix_softmax):
             fn.restype = ctypes.c_int
@@ -103,17 +103,25 @@ def feature_map(x, W, nthreads: int = 0) -> np.ndarray:
     return phi
 
 
+def _kv_heads(H: int, Hkv: int) -> int:
+    if Hkv <= 0 or H % Hkv:
+        raise OracleError(f"{H} query heads cannot share {Hkv} key/value heads evenly")
+    return Hkv
+
+
 def commit(S_pool, Z_pool, k, v, W, n_valid=None, slot=None, nthreads: int = 0):
-    """Fold k, v [B][H][T][d] into the pool states in place (section 3.1,
-    state update).  Returns the (fp64) S_pool, Z_pool arrays it updated."""
+    """Fold k, v [B][Hkv][T][d] into the pool states of the H = W.shape[0]
+    query heads (section 3.1, state update); query head h reads key/value head
+    h // (H // Hkv).  Returns the (fp64) S_pool, Z_pool arrays it updated."""
     S_pool, Z_pool = _f64(S_pool).copy(), _f64(Z_pool).copy()
     k, v, W = _f64(k), _f64(v), _f64(W)
-    B, H, T, d = k.shape
-    F = W.shape[2]
+    B, Hkv, T, d = k.shape
+    H, _, F = W.shape
+    _kv_heads(H, Hkv)
     assert v.shape == k.shape and W.shape == (H, d, F)
     assert S_pool.shape[1:] == (H, 2 * F, d) and Z_pool.shape[1:] == (H, 2 * F)
     nv, sl = _i32(n_valid), _i32(slot)
-    rc = _lib().orc_commit(B, H, T, d, F, _p(nv, _i32p), _p(k), _p(v), _p(W),
+    rc = _lib().orc_commit(B, H, Hkv, T, d, F, _p(nv, _i32p), _p(k), _p(v), _p(W),
                            _p(S_pool), _p(Z_pool), _p(sl, _i32p), nthreads)
     if rc:
         raise OracleError(f"orc_commit rc={rc}")
@@ -121,18 +129,20 @@ def commit(S_pool, Z_pool, k, v, W, n_valid=None, slot=None, nthreads: int = 0):
 
 
 def step(q, k, v, W, S_pool, Z_pool, gate=None, slot=None, nthreads: int = 0) -> np.ndarray:
-    """One block-hybrid denoising step; q, k, v [B][H][L][d] -> out [B][H][L][d]
-    (section 3.1: within-block softmax, linear readout, gated merge)."""
+    """One block-hybrid denoising step; q [B][H][L][d], k, v [B][Hkv][L][d]
+    -> out [B][H][L][d] (section 3.1: within-block softmax, linear readout,
+    gated merge).  Query head h reads key/value head h // (H // Hkv)."""
     q, k, v, W = _f64(q), _f64(k), _f64(v), _f64(W)
     S_pool, Z_pool = _f64(S_pool), _f64(Z_pool)
     B, H, L, d = q.shape
     F = W.shape[2]
-    assert k.shape == q.shape and v.shape == q.shape and W.shape == (H, d, F)
+    Hkv = _kv_heads(H, k.shape[1])
+    assert k.shape == (B, Hkv, L, d) and v.shape == k.shape and W.shape == (H, d, F)
     assert S_pool.shape[1:] == (H, 2 * F, d) and Z_pool.shape[1:] == (H, 2 * F)
     g = None if gate is None else _f64(gate)
     sl = _i32(slot)
     out = np.zeros((B, H, L, d))
-    rc = _lib().orc_step(B, H, L, d, F, _p(q), _p(k), _p(v), _p(W), _p(g),
+    rc = _lib().orc_step(B, H, Hkv, L, d, F, _p(q), _p(k), _p(v), _p(W), _p(g),
                          _p(S_pool), _p(Z_pool), _p(sl, _i32p), _p(out), nthreads)
     if rc:
         raise OracleError(f"orc_step rc={rc}")
@@ -141,14 +151,17 @@ def step(q, k, v, W, S_pool, Z_pool, gate=None, slot=None, nthreads: int = 0) ->
 
 def prefix_softmax(q, k, v, Kc, Vc, prefix_len=None, nthreads: int = 0) -> np.ndarray:
     """Full softmax attention of block queries over [prefix cache ; block]
-    (section 2.2, softmax attention): the comparator.  Kc, Vc [B][H][P][d]."""
+    (section 2.2, softmax attention): the comparator.  k, v [B][Hkv][L][d],
+    Kc, Vc [B][Hkv][P][d]; query head h reads key/value head h // (H // Hkv)."""
     q, k, v, Kc, Vc = _f64(q), _f64(k), _f64(v), _f64(Kc), _f64(Vc)
     B, H, L, d = q.shape
     P = Kc.shape[2]
-    assert Kc.shape == (B, H, P, d) and Vc.shape == Kc.shape
+    Hkv = _kv_heads(H, k.shape[1])
+    assert k.shape == (B, Hkv, L, d) and v.shape == k.shape
+    assert Kc.shape == (B, Hkv, P, d) and Vc.shape == Kc.shape
     pl = _i32(prefix_len)
     out = np.zeros((B, H, L, d))
-    rc = _lib().orc_prefix_softmax(B, H, L, d, P, _p(pl, _i32p), _p(q), _p(k), _p(v),
+    rc = _lib().orc_prefix_softmax(B, H, Hkv, L, d, P, _p(pl, _i32p), _p(q), _p(k), _p(v),
                                    _p(Kc), _p(Vc), _p(out), nthreads)
     if rc:
         raise OracleError(f"orc_prefix_softmax rc={rc}")

@@ -19,13 +19,20 @@
  * (request, head) pairs, which does not change any element's arithmetic.
  *
  * Layouts (row-major, C order):
- *   x, q, k, v, out   [B][H][L][d]        one block of L tokens per request
+ *   x, q, out         [B][H][L][d]        one block of L tokens per request
+ *   k, v              [B][Hkv][L][d]      key/value heads; query head h reads
+ *                                         key/value head h / (H / Hkv)
  *   W                 [H][d][F]           u = x W  (W is d x F, per head)
  *   gate              [H] or NULL         w = sigma(alpha); NULL means w = 1
  *   S pool            [n_slots][H][2F][d] S = sum phi(k) v^T
  *   Z pool            [n_slots][H][2F]    Z = sum phi(k)
  *   slot              [B] or NULL         request -> pool slot; NULL means b
- *   Kc, Vc            [B][H][P][d]        full prefix cache for the comparator
+ *   Kc, Vc            [B][Hkv][P][d]      full prefix cache for the comparator
+ *
+ * Query heads own W, the gate and the states (section 3.1, and section 3.3
+ * on serving, keep them per query head).  When Hkv < H, consecutive
+ * groups of H / Hkv query heads share one key/value head; Hkv == H is the
+ * plain multi-head case.
  *
  * Parity of each function is pinned by the CPU tests against closed forms,
  * a hand-worked example, library softmax/SDPA and brute-force Eq. 1.
@@ -37,6 +44,11 @@
 #ifdef _OPENMP
 #include <omp.h>
 #endif
+
+/* Key/value row block of query head h of request b. */
+static int64_t kv_index(int b, int h, int H, int Hkv) {
+    return (int64_t)b * Hkv + h / (H / Hkv);
+}
 
 /* Largest |score| for which exp() of the unshifted score stays far from fp64
  * overflow (exp(709) is the limit).  The step and comparator below use the
@@ -103,11 +115,11 @@ int orc_feature_map(int64_t n, int H, int d, int F, const double *x,
  *   Z_n = Z_{n-1} + sum_{t in block} phi(k_t).
  * Written token by token.  Request b folds its first n_valid[b] tokens
  * (all T when n_valid is NULL) into pool slot slot[b] (b when NULL). */
-int orc_commit(int B, int H, int T, int d, int F, const int32_t *n_valid,
+int orc_commit(int B, int H, int Hkv, int T, int d, int F, const int32_t *n_valid,
                const double *k, const double *v, const double *W,
                double *S_pool, double *Z_pool, const int32_t *slot,
                int nthreads) {
-    if (B < 0 || H <= 0 || T < 0 || d <= 0 || F <= 0) return 1;
+    if (B < 0 || H <= 0 || Hkv <= 0 || H % Hkv || T < 0 || d <= 0 || F <= 0) return 1;
     const int P2 = 2 * F;
     int nt = threads_or_default(nthreads);
     int bad = 0;
@@ -120,11 +132,12 @@ int orc_commit(int B, int H, int T, int d, int F, const int32_t *n_valid,
         double *S = S_pool + (s * H + h) * (int64_t)P2 * d;
         double *Z = Z_pool + (s * H + h) * (int64_t)P2;
         const double *Wh = W + (int64_t)h * d * F;
+        const int64_t kvh = kv_index(b, h, H, Hkv);
         double *u = (double *)malloc(sizeof(double) * F);
         double *p = (double *)malloc(sizeof(double) * P2);
         for (int t = 0; t < nv; ++t) {
-            const double *kt = k + (bh * T + t) * (int64_t)d;
-            const double *vt = v + (bh * T + t) * (int64_t)d;
+            const double *kt = k + (kvh * T + t) * (int64_t)d;
+            const double *vt = v + (kvh * T + t) * (int64_t)d;
             phi_row(d, F, kt, Wh, u, p);
             for (int f = 0; f < P2; ++f) {
                 Z[f] += p[f];
@@ -145,11 +158,11 @@ int orc_commit(int B, int H, int T, int d, int F, const int32_t *n_valid,
  *   gated merge          out = (w sm_num + lin_num) / (w sm_den + lin_den).
  * Scores are used unshifted, exactly as written; |score| above
  * ORC_MAX_ABS_SCORE is refused (return 3) instead of overflowing. */
-int orc_step(int B, int H, int L, int d, int F, const double *q,
+int orc_step(int B, int H, int Hkv, int L, int d, int F, const double *q,
              const double *k, const double *v, const double *W,
              const double *gate, const double *S_pool, const double *Z_pool,
              const int32_t *slot, double *out, int nthreads) {
-    if (B < 0 || H <= 0 || L <= 0 || d <= 0 || F <= 0) return 1;
+    if (B < 0 || H <= 0 || Hkv <= 0 || H % Hkv || L <= 0 || d <= 0 || F <= 0) return 1;
     const int P2 = 2 * F;
     const double scale = 1.0 / sqrt((double)d);
     int nt = threads_or_default(nthreads);
@@ -162,9 +175,10 @@ int orc_step(int B, int H, int L, int d, int F, const double *q,
         const double *Z = Z_pool + (s * H + h) * (int64_t)P2;
         const double *Wh = W + (int64_t)h * d * F;
         const double w = gate ? gate[h] : 1.0;
+        const int64_t kvh = kv_index(b, h, H, Hkv);
         const double *qb = q + bh * (int64_t)L * d;
-        const double *kb = k + bh * (int64_t)L * d;
-        const double *vb = v + bh * (int64_t)L * d;
+        const double *kb = k + kvh * (int64_t)L * d;
+        const double *vb = v + kvh * (int64_t)L * d;
         double *ob = out + bh * (int64_t)L * d;
         double *u = (double *)malloc(sizeof(double) * F);
         double *p = (double *)malloc(sizeof(double) * P2);
@@ -208,24 +222,25 @@ int orc_step(int B, int H, int L, int d, int F, const double *q,
  * block key visible to the block's queries): the comparator the hybrid
  * layer replaces.  Request b uses the first prefix_len[b] cached tokens
  * (max_prefix when NULL). */
-int orc_prefix_softmax(int B, int H, int L, int d, int max_prefix,
+int orc_prefix_softmax(int B, int H, int Hkv, int L, int d, int max_prefix,
                        const int32_t *prefix_len, const double *q,
                        const double *k, const double *v, const double *Kc,
                        const double *Vc, double *out, int nthreads) {
-    if (B < 0 || H <= 0 || L <= 0 || d <= 0 || max_prefix < 0) return 1;
+    if (B < 0 || H <= 0 || Hkv <= 0 || H % Hkv || L <= 0 || d <= 0 || max_prefix < 0) return 1;
     const double scale = 1.0 / sqrt((double)d);
     int nt = threads_or_default(nthreads);
     int bad = 0;
     #pragma omp parallel for num_threads(nt) schedule(dynamic) reduction(|:bad)
     for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
-        int b = (int)(bh / H);
+        int b = (int)(bh / H), h = (int)(bh % H);
         int P = prefix_len ? prefix_len[b] : max_prefix;
         if (P < 0 || P > max_prefix) { bad |= 2; continue; }
+        const int64_t kvh = kv_index(b, h, H, Hkv);
         const double *qb = q + bh * (int64_t)L * d;
-        const double *kb = k + bh * (int64_t)L * d;
-        const double *vb = v + bh * (int64_t)L * d;
-        const double *Kb = Kc + bh * (int64_t)max_prefix * d;
-        const double *Vb = Vc + bh * (int64_t)max_prefix * d;
+        const double *kb = k + kvh * (int64_t)L * d;
+        const double *vb = v + kvh * (int64_t)L * d;
+        const double *Kb = Kc + kvh * (int64_t)max_prefix * d;
+        const double *Vb = Vc + kvh * (int64_t)max_prefix * d;
         double *ob = out + bh * (int64_t)L * d;
         double *num = (double *)malloc(sizeof(double) * d);
         for (int i = 0; i < L; ++i) {

@@ -356,3 +356,75 @@ def test_comparator_ragged_prefix_and_empty_state_agreement():
     # at P = 0 the comparator and the hybrid step with an empty state are both block softmax
     hyb = oracle.step(q[1:2], k[1:2], v[1:2], W, *empty_pool(1, H, F, d))
     np.testing.assert_allclose(out[1], hyb[0], rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------- key/value head groups
+# Query heads own W, the gate and the states (section 3.1; section 3.3 keeps
+# the state per query head); consecutive groups of H / Hkv query heads read
+# one key/value head.  The library route is torch SDPA's own grouped-query
+# mode, and brute force indexes the key/value head by h // (H / Hkv).
+def gqa_case(rng, B, H, Hkv, L, d, F, P):
+    W = rng.normal(0, d ** -0.5, (H, d, F))
+    q = rng.normal(0, 1, (B, H, L, d))
+    k, v = (rng.normal(0, 1, (B, Hkv, L, d)) for _ in range(2))
+    pk, pv = (rng.normal(0, 1, (B, Hkv, P, d)) for _ in range(2))
+    return W, q, k, v, pk, pv
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 1), (4, 2), (6, 3)])
+def test_gqa_step_empty_state_is_grouped_sdpa(H, Hkv):
+    rng = np.random.default_rng(40 + H + Hkv)
+    B, L, d, F = 2, 16, 32, 8
+    W, q, k, v, _, _ = gqa_case(rng, B, H, Hkv, L, d, F, 0)
+    out = oracle.step(q, k, v, W, *empty_pool(B, H, F, d))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), enable_gqa=True).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 1), (4, 2)])
+def test_gqa_commit_equals_library_matmul(H, Hkv):
+    rng = np.random.default_rng(44 + Hkv)
+    B, T, d, F = 2, 24, 16, 8
+    W, _, k, v, _, _ = gqa_case(rng, B, H, Hkv, T, d, F, 0)
+    S, Z = oracle.commit(*empty_pool(B, H, F, d), k, v, W)
+    G = H // Hkv
+    for b in range(B):
+        for h in range(H):
+            p = lib_phi(k[b, h // G], W[h])                   # [T][2F]
+            np.testing.assert_allclose(S[b, h], p.T @ v[b, h // G], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(Z[b, h], p.sum(0), rtol=1e-12, atol=1e-13)
+
+
+def test_gqa_step_equals_brute_force_prefix():
+    rng = np.random.default_rng(46)
+    B, H, Hkv, L, d, F, P = 2, 4, 2, 8, 16, 8, 40
+    W, q, k, v, pk, pv = gqa_case(rng, B, H, Hkv, L, d, F, P)
+    gate = np.array([1.0, 0.4, 2.0, 0.7])
+    S, Z = oracle.commit(*empty_pool(B, H, F, d), pk, pv, W)
+    out = oracle.step(q, k, v, W, S, Z, gate=gate)
+    G = H // Hkv
+    for b in range(B):
+        for h in range(H):
+            g = h // G
+            ref = _brute_force_hybrid(q[b, h], k[b, g], v[b, g], W[h], pk[b, g], pv[b, g], gate[h])
+            np.testing.assert_allclose(out[b, h], ref, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("P", [0, 45])
+def test_gqa_comparator_is_grouped_sdpa(P):
+    rng = np.random.default_rng(48 + P)
+    B, H, Hkv, L, d = 2, 6, 2, 8, 16
+    _, q, k, v, pk, pv = gqa_case(rng, B, H, Hkv, L, d, 4, P)
+    out = oracle.prefix_softmax(q, k, v, pk, pv)
+    K = torch.from_numpy(np.concatenate([pk, k], 2))
+    V = torch.from_numpy(np.concatenate([pv, v], 2))
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), K, V, enable_gqa=True).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_gqa_rejects_uneven_groups():
+    rng = np.random.default_rng(50)
+    W, q, k, v, _, _ = gqa_case(rng, 1, 4, 3, 4, 8, 4, 0)
+    with pytest.raises(oracle.OracleError):
+        oracle.step(q, k, v, W, *empty_pool(1, 4, 4, 8))
