@@ -44,7 +44,7 @@ class Shape(ctypes.Structure):
     """Mirror of ``hba_shape``."""
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("feat", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
-                ("n_slots", ctypes.c_int64)]
+                ("n_slots", ctypes.c_int64), ("kv_heads", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -152,18 +152,28 @@ def feature_map(x: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = Non
     return out
 
 
+def _kv_heads(H, k):
+    """Key/value heads of k [B][Hkv][..][d]; H must be a multiple of it."""
+    Hkv = k.shape[1]
+    if Hkv <= 0 or H % Hkv:
+        raise ValueError(f"k: {Hkv} key/value heads do not divide {H} query heads")
+    return Hkv
+
+
 def step(q, k, v, W, S_pool, Z_pool, gate=None, slot=None, out=None, stream=None):
     """One block-hybrid denoising step (section 3.1).
 
-    q, k, v [B][H][L][d]; W [H][d][F]; S_pool [n_slots][H][2F][d] fp32;
+    q [B][H][L][d]; k, v [B][Hkv][L][d] with Hkv dividing H (query head h
+    reads key/value head h // (H // Hkv)); W [H][d][F]; S_pool [n_slots][H][2F][d] fp32;
     Z_pool [n_slots][H][2F] fp32; gate [H] fp32 (w = sigma(alpha)) or None;
     slot [B] int32 or None (request b uses slot b) -> out [B][H][L][d] fp32."""
     lib = load_library()
     B, H, L, d = q.shape
     F = W.shape[2]
     dt = _in_dtype(q, k, v, W)
+    Hkv = _kv_heads(H, k)
     for t, nm in ((k, "k"), (v, "v")):
-        _check(t, (B, H, L, d), q.dtype, nm)
+        _check(t, (B, Hkv, L, d), q.dtype, nm)
     _check(W, (H, d, F), q.dtype, "W")
     n_slots = S_pool.shape[0]
     _check(S_pool, (n_slots, H, 2 * F, d), torch.float32, "S_pool")
@@ -174,7 +184,7 @@ def step(q, k, v, W, S_pool, Z_pool, gate=None, slot=None, out=None, stream=None
         out = torch.empty((B, H, L, d), device=q.device, dtype=torch.float32)
     _check(out, (B, H, L, d), torch.float32, "out")
     _dev(q, k, v, W, S_pool, Z_pool, gate, slot, out)
-    shape = Shape(B, H, L, d, F, dt, n_slots)
+    shape = Shape(B, H, L, d, F, dt, n_slots, Hkv)
     _call(lib.hba_step, "hba_step", ctypes.byref(shape), _p(q), _p(k), _p(v), _p(W), _p(gate),
           _p(S_pool), _p(Z_pool), _p(slot), _p(out), _stream(stream))
     return out
@@ -189,8 +199,9 @@ def step_commit(q, k, v, W, S_pool, Z_pool, gate=None, slot=None, n_valid=None, 
     B, H, L, d = q.shape
     F = W.shape[2]
     dt = _in_dtype(q, k, v, W)
+    Hkv = _kv_heads(H, k)
     for t, nm in ((k, "k"), (v, "v")):
-        _check(t, (B, H, L, d), q.dtype, nm)
+        _check(t, (B, Hkv, L, d), q.dtype, nm)
     _check(W, (H, d, F), q.dtype, "W")
     n_slots = S_pool.shape[0]
     _check(S_pool, (n_slots, H, 2 * F, d), torch.float32, "S_pool")
@@ -202,21 +213,23 @@ def step_commit(q, k, v, W, S_pool, Z_pool, gate=None, slot=None, n_valid=None, 
         out = torch.empty((B, H, L, d), device=q.device, dtype=torch.float32)
     _check(out, (B, H, L, d), torch.float32, "out")
     _dev(q, k, v, W, S_pool, Z_pool, gate, slot, n_valid, out)
-    shape = Shape(B, H, L, d, F, dt, n_slots)
+    shape = Shape(B, H, L, d, F, dt, n_slots, Hkv)
     _call(lib.hba_step_commit, "hba_step_commit", ctypes.byref(shape), _p(n_valid), _p(q), _p(k), _p(v),
           _p(W), _p(gate), _p(S_pool), _p(Z_pool), _p(slot), _p(out), _stream(stream))
     return out
 
 
 def commit(k, v, W, S_pool, Z_pool, n_valid=None, slot=None, stream=None):
-    """Fold k, v [B][H][T][d] into the states in place (section 3.1):
-    S += sum_t phi(k_t) v_t^T, Z += sum_t phi(k_t) over the first n_valid[b]
-    tokens of each request (all T when n_valid is None)."""
+    """Fold k, v [B][Hkv][T][d] into the states of the H = W.shape[0] query
+    heads in place (section 3.1): S += sum_t phi(k_t) v_t^T, Z += sum_t phi(k_t)
+    over the first n_valid[b] tokens of each request (all T when n_valid is
+    None); query head h absorbs key/value head h // (H // Hkv)."""
     lib = load_library()
-    B, H, T, d = k.shape
-    F = W.shape[2]
+    B, Hkv, T, d = k.shape
+    H, F = W.shape[0], W.shape[2]
     dt = _in_dtype(k, v, W)
-    _check(v, (B, H, T, d), k.dtype, "v")
+    _kv_heads(H, k)
+    _check(v, (B, Hkv, T, d), k.dtype, "v")
     _check(W, (H, d, F), k.dtype, "W")
     n_slots = S_pool.shape[0]
     _check(S_pool, (n_slots, H, 2 * F, d), torch.float32, "S_pool")
@@ -224,29 +237,31 @@ def commit(k, v, W, S_pool, Z_pool, n_valid=None, slot=None, stream=None):
     _check(n_valid, (B,), torch.int32, "n_valid")
     _check(slot, (B,), torch.int32, "slot")
     _dev(k, v, W, S_pool, Z_pool, n_valid, slot)
-    shape = Shape(B, H, 1, d, F, dt, n_slots)
+    shape = Shape(B, H, 1, d, F, dt, n_slots, Hkv)
     _call(lib.hba_commit, "hba_commit", ctypes.byref(shape), T, _p(n_valid), _p(k), _p(v), _p(W),
           _p(S_pool), _p(Z_pool), _p(slot), _stream(stream))
 
 
 def prefix_softmax(q, k, v, Kc, Vc, prefix_len=None, out=None, stream=None):
     """Comparator: full softmax attention (section 2.2) of the block queries
-    over [prefix cache ; block].  q, k, v [B][H][L][d]; Kc, Vc [B][H][P][d]
-    (same dtype); prefix_len [B] int32 or None (all P)."""
+    over [prefix cache ; block].  q [B][H][L][d]; k, v [B][Hkv][L][d];
+    Kc, Vc [B][Hkv][P][d] (same dtype), Hkv dividing H; prefix_len [B] int32
+    or None (all P)."""
     lib = load_library()
     B, H, L, d = q.shape
     P = Kc.shape[2]
     dt = _in_dtype(q, k, v, Kc, Vc)
+    Hkv = _kv_heads(H, k)
     for t, nm in ((k, "k"), (v, "v")):
-        _check(t, (B, H, L, d), q.dtype, nm)
-    _check(Kc, (B, H, P, d), q.dtype, "Kc")
-    _check(Vc, (B, H, P, d), q.dtype, "Vc")
+        _check(t, (B, Hkv, L, d), q.dtype, nm)
+    _check(Kc, (B, Hkv, P, d), q.dtype, "Kc")
+    _check(Vc, (B, Hkv, P, d), q.dtype, "Vc")
     _check(prefix_len, (B,), torch.int32, "prefix_len")
     if out is None:
         out = torch.empty((B, H, L, d), device=q.device, dtype=torch.float32)
     _check(out, (B, H, L, d), torch.float32, "out")
     _dev(q, k, v, Kc, Vc, prefix_len, out)
-    shape = Shape(B, H, L, d, 64, dt, 0)
+    shape = Shape(B, H, L, d, 64, dt, 0, Hkv)
     kc = _p(Kc) if P > 0 else None
     vc = _p(Vc) if P > 0 else None
     _call(lib.hba_prefix_softmax, "hba_prefix_softmax", ctypes.byref(shape), P, _p(prefix_len), _p(q),

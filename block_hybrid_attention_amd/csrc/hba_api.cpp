@@ -28,6 +28,14 @@ hba_status check_common(const hba_shape *s, bool need_block, bool need_feat) {
     return HBA_OK;
 }
 
+// Query heads per key/value head, or 0 when kv_heads is negative or does not
+// divide heads.
+int kv_group(const hba_shape *s) {
+    const int hkv = s->kv_heads == 0 ? s->heads : s->kv_heads;
+    if (hkv < 0 || hkv > s->heads || s->heads % hkv) return 0;
+    return s->heads / hkv;
+}
+
 hba_status from_hip(hipError_t e) { return e == hipSuccess ? HBA_OK : HBA_ERR_HIP; }
 
 }  // namespace
@@ -48,7 +56,7 @@ const char *hba_status_string(hba_status st) {
     return "unknown status";
 }
 
-int32_t hba_abi_version(void) { return 2; }
+int32_t hba_abi_version(void) { return 3; }
 
 hba_status hba_feature_map(const hba_shape *shape, int64_t n_rows, const void *x, const void *W,
                            float *phi, void *stream) {
@@ -69,14 +77,15 @@ hba_status hba_step(const hba_shape *shape, const void *q, const void *k, const 
                     const int32_t *slot, float *out, void *stream) {
     hba_status st = check_common(shape, true, true);
     if (st != HBA_OK) return st;
-    if (shape->n_slots < 0) return HBA_ERR_SHAPE;
+    const int G = kv_group(shape);
+    if (shape->n_slots < 0 || G == 0) return HBA_ERR_SHAPE;
     if (shape->batch == 0) return HBA_OK;
     if (!q || !k || !v || !W || !S_pool || !Z_pool || !out) return HBA_ERR_NULL;
     if (!slot && shape->batch > shape->n_slots) return HBA_ERR_CAPACITY;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(W) || !aligned16(S_pool) ||
         !aligned16(Z_pool) || !aligned16(out) || (gate && !aligned4(gate)) || (slot && !aligned4(slot)))
         return HBA_ERR_ALIGN;
-    hba::StepArgs a{q, k, v, W, gate, S_pool, Z_pool, slot, out, shape->batch, shape->heads, shape->block};
+    hba::StepArgs a{q, k, v, W, gate, S_pool, Z_pool, slot, out, shape->batch, shape->heads, shape->block, G};
     return from_hip(hba::launch_step(a, shape->in_dtype == HBA_BF16, shape->head_dim, shape->feat,
                                      static_cast<hipStream_t>(stream)));
 }
@@ -86,14 +95,15 @@ hba_status hba_commit(const hba_shape *shape, int32_t n_tok, const int32_t *n_va
                       void *stream) {
     hba_status st = check_common(shape, false, true);
     if (st != HBA_OK) return st;
-    if (n_tok < 0 || shape->n_slots < 0) return HBA_ERR_SHAPE;
+    const int G = kv_group(shape);
+    if (n_tok < 0 || shape->n_slots < 0 || G == 0) return HBA_ERR_SHAPE;
     if (shape->batch == 0 || n_tok == 0) return HBA_OK;
     if (!k || !v || !W || !S_pool || !Z_pool) return HBA_ERR_NULL;
     if (!slot && shape->batch > shape->n_slots) return HBA_ERR_CAPACITY;
     if (!aligned16(k) || !aligned16(v) || !aligned16(W) || !aligned16(S_pool) || !aligned16(Z_pool) ||
         (n_valid && !aligned4(n_valid)) || (slot && !aligned4(slot)))
         return HBA_ERR_ALIGN;
-    hba::CommitArgs a{n_valid, k, v, W, S_pool, Z_pool, slot, shape->batch, shape->heads, n_tok};
+    hba::CommitArgs a{n_valid, k, v, W, S_pool, Z_pool, slot, shape->batch, shape->heads, n_tok, G};
     return from_hip(hba::launch_commit(a, shape->in_dtype == HBA_BF16, shape->head_dim, shape->feat,
                                        static_cast<hipStream_t>(stream)));
 }
@@ -103,7 +113,8 @@ hba_status hba_step_commit(const hba_shape *shape, const int32_t *n_valid, const
                            const int32_t *slot, float *out, void *stream) {
     hba_status st = check_common(shape, true, true);
     if (st != HBA_OK) return st;
-    if (shape->n_slots < 0) return HBA_ERR_SHAPE;
+    const int G = kv_group(shape);
+    if (shape->n_slots < 0 || G == 0) return HBA_ERR_SHAPE;
     if (shape->batch == 0) return HBA_OK;
     if (!q || !k || !v || !W || !S_pool || !Z_pool || !out) return HBA_ERR_NULL;
     if (!slot && shape->batch > shape->n_slots) return HBA_ERR_CAPACITY;
@@ -112,7 +123,7 @@ hba_status hba_step_commit(const hba_shape *shape, const int32_t *n_valid, const
         (n_valid && !aligned4(n_valid)))
         return HBA_ERR_ALIGN;
     hba::StepCommitArgs a{q, k, v, W, gate, S_pool, Z_pool, slot, n_valid, out, shape->batch, shape->heads,
-                          shape->block};
+                          shape->block, G};
     return from_hip(hba::launch_step_commit(a, shape->in_dtype == HBA_BF16, shape->head_dim, shape->feat,
                                             static_cast<hipStream_t>(stream)));
 }
@@ -122,14 +133,15 @@ hba_status hba_prefix_softmax(const hba_shape *shape, int32_t max_prefix, const 
                               const void *Vc, float *out, void *stream) {
     hba_status st = check_common(shape, true, false);
     if (st != HBA_OK) return st;
-    if (max_prefix < 0 || (int64_t)max_prefix + shape->block > 0x7fffffff) return HBA_ERR_SHAPE;
+    const int G = kv_group(shape);
+    if (max_prefix < 0 || (int64_t)max_prefix + shape->block > 0x7fffffff || G == 0) return HBA_ERR_SHAPE;
     if (shape->batch == 0) return HBA_OK;
     if (!q || !k || !v || !out) return HBA_ERR_NULL;
     if (max_prefix > 0 && (!Kc || !Vc)) return HBA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
         (max_prefix > 0 && (!aligned16(Kc) || !aligned16(Vc))) || (prefix_len && !aligned4(prefix_len)))
         return HBA_ERR_ALIGN;
-    hba::PrefixArgs a{prefix_len, q, k, v, Kc, Vc, out, shape->batch, shape->heads, shape->block, max_prefix};
+    hba::PrefixArgs a{prefix_len, q, k, v, Kc, Vc, out, shape->batch, shape->heads, shape->block, max_prefix, G};
     return from_hip(hba::launch_prefix_softmax(a, shape->in_dtype == HBA_BF16, shape->head_dim,
                                                static_cast<hipStream_t>(stream)));
 }

@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(CommitArgs a) {
     nv = nv < 0 ? 0 : (nv > T_ ? T_ : nv);
     const int64_t slot = a.slot ? (int64_t)a.slot[b] : (int64_t)b;
 
-    const T *kg = static_cast<const T *>(a.k) + (int64_t)bh * T_ * D;
-    const T *vg = static_cast<const T *>(a.v) + (int64_t)bh * T_ * D;
+    const T *kg = static_cast<const T *>(a.k) + (int64_t)(bh / a.G) * T_ * D;
+    const T *vg = static_cast<const T *>(a.v) + (int64_t)(bh / a.G) * T_ * D;
     const T *Wg = static_cast<const T *>(a.W) + (int64_t)h * D * F;
     float *Sg = a.S + (slot * a.H + h) * (int64_t)(2 * F) * D;
     float *Zg = a.Z + (slot * a.H + h) * (int64_t)(2 * F);
@@ -243,8 +243,8 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
     nv = nv < 0 ? 0 : (nv > T_ ? T_ : nv);
     if (nv == 0) return;   // nothing to fold; the state is left untouched
     const int64_t slot = a.slot ? (int64_t)a.slot[b] : (int64_t)b;
-    const T *kg = static_cast<const T *>(a.k) + (int64_t)bh * T_ * D;
-    const T *vg = static_cast<const T *>(a.v) + (int64_t)bh * T_ * D;
+    const T *kg = static_cast<const T *>(a.k) + (int64_t)(bh / a.G) * T_ * D;
+    const T *vg = static_cast<const T *>(a.v) + (int64_t)(bh / a.G) * T_ * D;
     const T *Wg = static_cast<const T *>(a.W) + (int64_t)h * D * F;
     float *Sg = a.S + ((slot * a.H + h) * (int64_t)(2 * F) + (int64_t)half * F) * D;
     float *Zg = a.Z + (slot * a.H + h) * (int64_t)(2 * F) + half * F;

@@ -16,8 +16,12 @@ struct FeatureMapArgs {
     int H;
 };
 
+// Key/value inputs are [B][H/G][...][d]: query head h of request b reads
+// key/value row block (b H + h) / G = b (H/G) + h / G.  G = 1 is plain
+// multi-head attention.
 struct StepArgs {
-    const void *q, *k, *v;   // [B][H][L][d]
+    const void *q;           // [B][H][L][d]
+    const void *k, *v;       // [B][H/G][L][d]
     const void *W;           // [H][d][F]
     const float *gate;       // [H] or null
     const float *S;          // [slots][H][2F][d]
@@ -25,10 +29,12 @@ struct StepArgs {
     const int32_t *slot;     // [B] or null
     float *out;              // [B][H][L][d]
     int B, H, L;
+    int G;                   // query heads per key/value head
 };
 
 struct StepCommitArgs {
-    const void *q, *k, *v;   // [B][H][L][d]
+    const void *q;           // [B][H][L][d]
+    const void *k, *v;       // [B][H/G][L][d]
     const void *W;           // [H][d][F]
     const float *gate;       // [H] or null
     float *S;                // [slots][H][2F][d], updated in place
@@ -37,23 +43,27 @@ struct StepCommitArgs {
     const int32_t *n_valid;  // [B] or null
     float *out;              // [B][H][L][d]
     int B, H, L;
+    int G;
 };
 struct CommitArgs {
     const int32_t *n_valid;  // [B] or null
-    const void *k, *v;       // [B][H][T][d]
+    const void *k, *v;       // [B][H/G][T][d]
     const void *W;           // [H][d][F]
     float *S;                // [slots][H][2F][d]
     float *Z;                // [slots][H][2F]
     const int32_t *slot;     // [B] or null
     int B, H, T;
+    int G;
 };
 
 struct PrefixArgs {
     const int32_t *prefix_len;  // [B] or null
-    const void *q, *k, *v;      // [B][H][L][d]
-    const void *Kc, *Vc;        // [B][H][P][d]
+    const void *q;              // [B][H][L][d]
+    const void *k, *v;          // [B][H/G][L][d]
+    const void *Kc, *Vc;        // [B][H/G][P][d]
     float *out;                 // [B][H][L][d]
     int B, H, L, P;
+    int G;
 };
 
 // Enqueue kernel `k` with a single by-value argument block on `stream`; the

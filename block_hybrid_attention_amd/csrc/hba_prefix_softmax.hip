@@ -36,25 +36,26 @@ struct PrefixOps {
 };
 
 template <typename T, int D>
-__device__ __forceinline__ const T *key_row(const PrefixArgs &a, int64_t bh, int P, int j) {
-    // virtual concatenation [prefix cache ; block]; caller clamps j < P + L
-    return j < P ? static_cast<const T *>(a.Kc) + (bh * a.P + j) * D
-                 : static_cast<const T *>(a.k) + (bh * a.L + (j - P)) * D;
+__device__ __forceinline__ const T *key_row(const PrefixArgs &a, int64_t kvh, int P, int j) {
+    // virtual concatenation [prefix cache ; block] of key/value row block kvh;
+    // caller clamps j < P + L
+    return j < P ? static_cast<const T *>(a.Kc) + (kvh * a.P + j) * D
+                 : static_cast<const T *>(a.k) + (kvh * a.L + (j - P)) * D;
 }
 template <typename T, int D>
-__device__ __forceinline__ const T *val_row(const PrefixArgs &a, int64_t bh, int P, int j) {
-    return j < P ? static_cast<const T *>(a.Vc) + (bh * a.P + j) * D
-                 : static_cast<const T *>(a.v) + (bh * a.L + (j - P)) * D;
+__device__ __forceinline__ const T *val_row(const PrefixArgs &a, int64_t kvh, int P, int j) {
+    return j < P ? static_cast<const T *>(a.Vc) + (kvh * a.P + j) * D
+                 : static_cast<const T *>(a.v) + (kvh * a.L + (j - P)) * D;
 }
 
 template <typename T, int D>
-__device__ __forceinline__ void load_tile(const PrefixArgs &a, int64_t bh, int P, int nkeys, int j0,
+__device__ __forceinline__ void load_tile(const PrefixArgs &a, int64_t kvh, int P, int nkeys, int j0,
                                           int li, int lg, PrefixOps<T, D> &op) {
     using O = PrefixOps<T, D>;
     // K row for this lane: key j0 + li (clamped; masked later)
     int jk = j0 + li;
     jk = jk < nkeys ? jk : nkeys - 1;
-    const T *kr = key_row<T, D>(a, bh, P, jk);
+    const T *kr = key_row<T, D>(a, kvh, P, jk);
     if constexpr (O::kBf16) {
 #pragma unroll
         for (int s = 0; s < D / 32; ++s) op.kq[s] = *reinterpret_cast<const uint4 *>(kr + 32 * s + 8 * lg);
@@ -67,7 +68,7 @@ __device__ __forceinline__ void load_tile(const PrefixArgs &a, int64_t bh, int P
     for (int r = 0; r < 4; ++r) {
         int jv = j0 + 4 * lg + r;
         jv = jv < nkeys ? jv : nkeys - 1;
-        const T *vr = val_row<T, D>(a, bh, P, jv) + O::NCT * li;
+        const T *vr = val_row<T, D>(a, kvh, P, jv) + O::NCT * li;
         if constexpr (O::VBYTES >= 16) {
 #pragma unroll
             for (int q = 0; q < O::VBYTES / 16; ++q) op.vq[r][q] = reinterpret_cast<const uint4 *>(vr)[q];
@@ -112,6 +113,7 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(PrefixArgs a) {
     const int lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const int64_t bh = blockIdx.x;
+    const int64_t kvh = bh / a.G;
     const int b = (int)(bh / a.H);
     const int L = a.L;
     int P = a.prefix_len ? a.prefix_len[b] : a.P;
@@ -145,13 +147,13 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(PrefixArgs a) {
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
     PrefixOps<T, D> cur, nxt;
-    if (wave < ntiles) load_tile<T, D>(a, bh, P, nkeys, 16 * wave, li, lg, cur);
+    if (wave < ntiles) load_tile<T, D>(a, kvh, P, nkeys, 16 * wave, li, lg, cur);
 #pragma unroll 1
     for (int tile = wave; tile < ntiles; tile += 4) {
         const int j0 = 16 * tile;
         {   // prefetch the wave's next tile (clamped to the last one)
             const int tn = tile + 4 < ntiles ? tile + 4 : ntiles - 1;
-            load_tile<T, D>(a, bh, P, nkeys, 16 * tn, li, lg, nxt);
+            load_tile<T, D>(a, kvh, P, nkeys, 16 * tn, li, lg, nxt);
         }
         floatx4 s[2];
 #pragma unroll
@@ -277,6 +279,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel_bf16(PrefixArgs a) 
     const int lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const int64_t bh = blockIdx.x;
+    const int64_t kvh = bh / a.G;
     const int b = (int)(bh / a.H);
     const int L = a.L;
     int P = a.prefix_len ? a.prefix_len[b] : a.P;
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel_bf16(PrefixArgs a) 
         for (int hh = 0; hh < 2; ++hh) {
             int jk = j0 + 16 * hh + li;
             jk = jk < nkeys ? jk : nkeys - 1;
-            const T *kr = key_row<T, D>(a, bh, P, jk) + 8 * lg;
+            const T *kr = key_row<T, D>(a, kvh, P, jk) + 8 * lg;
 #pragma unroll
             for (int s_ = 0; s_ < KS; ++s_) t.k[hh][s_] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kr + 32 * s_));
         }
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel_bf16(PrefixArgs a) 
             for (int e = 0; e < 8; ++e) {
                 int jv = j0 + (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4);
                 jv = jv < nkeys ? jv : nkeys - 1;
-                const T *vr = val_row<T, D>(a, bh, P, jv) + 8 * li;
+                const T *vr = val_row<T, D>(a, kvh, P, jv) + 8 * li;
                 t.v[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vr));
             }
         }

@@ -161,8 +161,8 @@ __global__ __launch_bounds__(kThreads, 3) void step_kernel_f32(StepArgs a) {
     const int64_t slot = a.slot ? (int64_t)a.slot[b] : (int64_t)b;
 
     const T *qg = static_cast<const T *>(a.q) + (int64_t)bh * L * D;
-    const T *kg = static_cast<const T *>(a.k) + (int64_t)bh * L * D;
-    const T *vg = static_cast<const T *>(a.v) + (int64_t)bh * L * D;
+    const T *kg = static_cast<const T *>(a.k) + (int64_t)(bh / a.G) * L * D;
+    const T *vg = static_cast<const T *>(a.v) + (int64_t)(bh / a.G) * L * D;
     const T *Wg = static_cast<const T *>(a.W) + (int64_t)h * D * F;
     const float *Sg = a.S + (slot * a.H + h) * (int64_t)(2 * F) * D;
     const float *Zg = a.Z + (slot * a.H + h) * (int64_t)(2 * F);
@@ -423,8 +423,8 @@ __global__ __launch_bounds__(kThreads, 3) void step_kernel_bf16(StepArgs a) {
     const int64_t slot = a.slot ? (int64_t)a.slot[b] : (int64_t)b;
 
     const T *qg = static_cast<const T *>(a.q) + (int64_t)bh * L * D;
-    const T *kg = static_cast<const T *>(a.k) + (int64_t)bh * L * D;
-    const T *vg = static_cast<const T *>(a.v) + (int64_t)bh * L * D;
+    const T *kg = static_cast<const T *>(a.k) + (int64_t)(bh / a.G) * L * D;
+    const T *vg = static_cast<const T *>(a.v) + (int64_t)(bh / a.G) * L * D;
     const T *Wg = static_cast<const T *>(a.W) + (int64_t)h * D * F;
     const float *Sg = a.S + (slot * a.H + h) * (int64_t)(2 * F) * D;
     const float *Zg = a.Z + (slot * a.H + h) * (int64_t)(2 * F);

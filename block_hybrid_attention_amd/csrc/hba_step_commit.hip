@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kFusedThreads, 2) void step_commit_kernel_bf16(Step
     const int64_t slot = a.slot ? (int64_t)a.slot[b] : (int64_t)b;
 
     const T *qg = static_cast<const T *>(a.q) + (int64_t)bh * L * D;
-    const T *kg = static_cast<const T *>(a.k) + (int64_t)bh * L * D;
-    const T *vg = static_cast<const T *>(a.v) + (int64_t)bh * L * D;
+    const T *kg = static_cast<const T *>(a.k) + (int64_t)(bh / a.G) * L * D;
+    const T *vg = static_cast<const T *>(a.v) + (int64_t)(bh / a.G) * L * D;
     const T *Wg = static_cast<const T *>(a.W) + (int64_t)h * D * F;
     float *Sg = a.S + (slot * a.H + h) * (int64_t)(2 * F) * D;
     float *Zg = a.Z + (slot * a.H + h) * (int64_t)(2 * F);
@@ -376,10 +376,10 @@ hipError_t launch_step_commit(const StepCommitArgs &a, bool bf16, int d, int F, 
             return launch_kernel(step_commit_kernel_bf16<128, 64>, dim3((unsigned)(a.B * a.H)), dim3(kFusedThreads), a, stream);
     }
     // other shapes: the step on the current state, then the commit
-    const StepArgs s{a.q, a.k, a.v, a.W, a.gate, a.S, a.Z, a.slot, a.out, a.B, a.H, a.L};
+    const StepArgs s{a.q, a.k, a.v, a.W, a.gate, a.S, a.Z, a.slot, a.out, a.B, a.H, a.L, a.G};
     hipError_t e = launch_step(s, bf16, d, F, stream);
     if (e != hipSuccess) return e;
-    const CommitArgs c{a.n_valid, a.k, a.v, a.W, a.S, a.Z, a.slot, a.B, a.H, a.L};
+    const CommitArgs c{a.n_valid, a.k, a.v, a.W, a.S, a.Z, a.slot, a.B, a.H, a.L, a.G};
     return launch_commit(c, bf16, d, F, stream);
 }
 

@@ -20,7 +20,8 @@
  *     the device surfaces at the caller's next synchronisation.
  *   - Host-checkable problems return a status and launch nothing: NULL
  *     pointers, non-positive or too-large sizes, unsupported (d, F, L, dtype),
- *     pointers not aligned to 16 bytes.  A launch failure returns
+ *     pointers not aligned to 16 bytes, kv_heads that is negative or does not
+ *     divide heads.  A launch failure returns
  *     HBA_ERR_HIP.
  *   - Values that live on the device (slot indices, per-request lengths, gate
  *     values) cannot be checked without a synchronisation, so their ranges are
@@ -30,6 +31,14 @@
  *     elements.
  *   - Supported shapes: head_dim d in {64, 128}; feat F in {64, 128} (the
  *     feature map has 2F entries); block L in [1, 32]; heads H >= 1.
+ *   - Key/value head groups.  W, the gate, S and Z belong to query heads
+ *     (section 3.1 learns W and the gate per query head; section 3.3 stores
+ *     the state per query head beside the paged KV cache).  Keys and values
+ *     may have fewer heads, Hkv = kv_heads, with H a multiple of Hkv:
+ *     query head h then reads key/value head h / (H / Hkv), so consecutive
+ *     groups of H / Hkv query heads share one (grouped-query attention).
+ *     kv_heads = 0 or kv_heads = heads is plain multi-head attention.  The
+ *     pages do not spell out the grouping; this is the common convention.
  *   - in_dtype selects the element type of q, k, v, x, W, Kc and Vc:
  *     HBA_F32 (float) or HBA_BF16 (bfloat16 stored as uint16).  States S, Z,
  *     feature-map output and attention outputs are always fp32; every
@@ -70,6 +79,7 @@ typedef struct {
     int32_t feat;      /* F: 64 or 128; phi(x) has 2F entries */
     int32_t in_dtype;  /* hba_dtype of q, k, v, x, W, Kc, Vc */
     int64_t n_slots;   /* slots in the S/Z pool (hba_step, hba_commit) */
+    int32_t kv_heads;  /* Hkv: key/value heads, dividing H; 0 means H */
 } hba_shape;
 
 /* Hedgehog feature map (section 3.1):
@@ -92,8 +102,9 @@ hba_status hba_feature_map(const hba_shape *shape, int64_t n_rows, const void *x
  *   out_i   = (w sm_num + lin_num) / (w sm_den + lin_den),  w = gate[h]
  * The kernels apply one exponent shift per query to both branches, which
  * leaves the ratio unchanged and keeps every term finite.
- * Reads: batch, heads, block, head_dim, feat, in_dtype, n_slots.
- *   q, k, v  [B][H][L][d]        in_dtype, the active block
+ * Reads: batch, heads, block, head_dim, feat, in_dtype, n_slots, kv_heads.
+ *   q        [B][H][L][d]        in_dtype, the active block's queries
+ *   k, v     [B][Hkv][L][d]      in_dtype, the active block's keys/values
  *   W        [H][d][F]           in_dtype
  *   gate     [H] fp32 or NULL    w = sigma(alpha) per head; NULL means w = 1.
  *                                Precondition: 0 < w < inf.
@@ -113,10 +124,12 @@ hba_status hba_step(const hba_shape *shape, const void *q, const void *k, const 
  * over the first n_valid[b] of the n_tok tokens passed for request b.
  * Any n_tok >= 0 is accepted: a block, several blocks, or a whole prefix in
  * one call; by associativity the result does not depend on the chunking.
- * Reads: batch, heads, head_dim, feat, in_dtype, n_slots (block is ignored).
+ * Reads: batch, heads, head_dim, feat, in_dtype, n_slots, kv_heads (block is
+ * ignored).  The state of query head h absorbs key/value head h / (H / Hkv)
+ * mapped through that query head's own W.
  *   n_valid  [B] int32 or NULL   tokens to fold per request; NULL means n_tok.
  *                                Precondition: 0 <= n_valid[b] <= n_tok.
- *   k, v     [B][H][n_tok][d]    in_dtype
+ *   k, v     [B][Hkv][n_tok][d]  in_dtype
  *   W        [H][d][F]           in_dtype
  *   S_pool   [n_slots][H][2F][d] fp32, updated in place
  *   Z_pool   [n_slots][H][2F]    fp32, updated in place
@@ -137,7 +150,7 @@ hba_status hba_commit(const hba_shape *shape, int32_t n_tok, const int32_t *n_va
  * with the block's own keys and values.  For bf16 inputs with head_dim 128
  * it is one kernel that reads S once and writes it once; other shapes run
  * the step kernel and then the commit kernel.
- * Reads: batch, heads, block, head_dim, feat, in_dtype, n_slots.
+ * Reads: batch, heads, block, head_dim, feat, in_dtype, n_slots, kv_heads.
  *   n_valid  [B] int32 or NULL   tokens of the block to fold; NULL means the
  *                                whole block.  Precondition: 0 <= n_valid[b] <= block.
  *   q, k, v, W, gate, slot, out  as for hba_step
@@ -153,12 +166,14 @@ hba_status hba_step_commit(const hba_shape *shape, const int32_t *n_valid, const
  * queries over the request's cached prefix followed by the block itself,
  * scale 1/sqrt(d), every key visible, no gate -- the prefix attention that
  * block-hybrid attention replaces with a fixed-size state.
- * Reads: batch, heads, block, head_dim, in_dtype (feat and n_slots ignored).
+ * Reads: batch, heads, block, head_dim, in_dtype, kv_heads (feat and n_slots
+ * ignored).
  *   prefix_len [B] int32 or NULL  cached tokens used by request b; NULL means
  *                                 max_prefix.  Precondition:
  *                                 0 <= prefix_len[b] <= max_prefix.
- *   q, k, v    [B][H][L][d]       in_dtype, the active block
- *   Kc, Vc     [B][H][max_prefix][d] in_dtype, the prefix cache; may be NULL
+ *   q          [B][H][L][d]       in_dtype, the active block's queries
+ *   k, v       [B][Hkv][L][d]     in_dtype, the active block's keys/values
+ *   Kc, Vc     [B][Hkv][max_prefix][d] in_dtype, the prefix cache; may be NULL
  *                                 only when max_prefix == 0
  *   out        [B][H][L][d]       fp32 output */
 hba_status hba_prefix_softmax(const hba_shape *shape, int32_t max_prefix,
@@ -169,7 +184,8 @@ hba_status hba_prefix_softmax(const hba_shape *shape, int32_t max_prefix,
 /* Static description of a status code (never NULL). */
 const char *hba_status_string(hba_status status);
 
-/* Library ABI version, currently 2 (2 added hba_step_commit). */
+/* Library ABI version, currently 3 (2 added hba_step_commit, 3 added
+ * hba_shape.kv_heads). */
 int32_t hba_abi_version(void);
 
 #ifdef __cplusplus

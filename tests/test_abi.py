@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol():
     L = lib()
     for n in names:
         assert hasattr(L, n), n
-    assert hba.abi_version() == 2
+    assert hba.abi_version() == 3
 
 
 def test_status_strings():
@@ -52,8 +52,8 @@ def test_status_strings():
     assert L.hba_status_string(99) == b"unknown status"
 
 
-def shape(batch=2, heads=4, block=32, d=128, F=128, dtype=1, slots=8):
-    return hba.Shape(batch, heads, block, d, F, dtype, slots)
+def shape(batch=2, heads=4, block=32, d=128, F=128, dtype=1, slots=8, kv_heads=0):
+    return hba.Shape(batch, heads, block, d, F, dtype, slots, kv_heads)
 
 
 A = ctypes.c_void_p(0x10000)      # aligned, never dereferenced
@@ -148,6 +148,30 @@ def test_prefix_and_feature_map_validation():
     assert L.hba_feature_map(ctypes.byref(sh), 10, None, A, A2, None) == ENULL
     assert L.hba_feature_map(ctypes.byref(shape(F=96)), 10, A, A, A2, None) == EUNSUP
     assert L.hba_feature_map(ctypes.byref(sh), 10, A, MIS, A2, None) == EALIGN
+
+
+@no_gpu_only
+def test_kv_heads_validation():
+    # kv_heads must divide heads (0 means heads); checked before any pointer
+    L = lib()
+    for bad in (-1, 3, 8):
+        sh = shape(heads=4, kv_heads=bad)
+        assert step_call(sh) == ESHAPE
+        assert L.hba_commit(ctypes.byref(sh), 32, None, A, A, A, A2, A2, None, None) == ESHAPE
+        assert L.hba_step_commit(ctypes.byref(sh), None, A, A, A, A, None, A2, A2, None, A2, None) == ESHAPE
+        assert L.hba_prefix_softmax(ctypes.byref(sh), 64, None, A, A, A, A, A, A2, None) == ESHAPE
+    # the feature map has no key/value heads and ignores the field
+    assert L.hba_feature_map(ctypes.byref(shape(kv_heads=3)), 0, None, None, None, None) == OK
+    for good in (1, 2, 4):
+        assert step_call(shape(batch=0, heads=4, kv_heads=good), q=None) == OK
+
+
+def test_python_binding_refuses_uneven_head_groups():
+    lib()
+    q = torch.zeros(1, 4, 8, 64)
+    k = torch.zeros(1, 3, 8, 64)
+    with pytest.raises(ValueError, match="key/value heads"):
+        hba.step(q, k, k, torch.zeros(4, 64, 64), torch.zeros(1, 4, 128, 64), torch.zeros(1, 4, 128))
 
 
 def test_python_binding_refuses_host_tensors():
