@@ -116,11 +116,13 @@ def _time_launches(torch, fn, warmup, iters, stream):
     return e0.elapsed_time(e1) / iters
 
 
-def comparator_sweep(args, torch, hba, wl, dev):
+def comparator_sweep(args, torch, hba, wl, dev, B=128):
     """Full softmax attention over a P-token bf16 KV cache (the layer the
     hybrid replaces) against the hybrid step reading the fixed-size state
-    built from the same cache: 128 requests, 16 heads, d=128, block 32."""
-    B, H, L, d, F = 128, 16, 32, 128, 128
+    built from the same cache: B requests, 16 heads, d=128, block 32.  Below
+    one (request, head) pair per compute unit the comparator is also timed
+    with its keys split over workgroups (the library's choice, and a sweep)."""
+    H, L, d, F = 16, 32, 128, 128
     dt = torch.bfloat16
     stream = torch.cuda.current_stream()
     rows = []
@@ -140,11 +142,28 @@ def comparator_sweep(args, torch, hba, wl, dev):
         hm = _time_launches(torch, lambda: hba.step(q, k, v, W, S, Z, out=out_h), 3, n, stream)
         kv_bytes = 2 * B * H * P * d * 2
         c_bytes = kv_bytes + 3 * B * H * L * d * 2 + B * H * L * d * 4
-        rows.append({"prefix": P, "comparator_ms": cm,
-                     "comparator_GBps": c_bytes / (cm * 1e-3) / 1e9,
-                     "hybrid_ms": hm,
-                     "hybrid_GBps": step_bytes(B, H, L, d, F) / (hm * 1e-3) / 1e9,
-                     "speedup": cm / hm, "comparator_kv_bytes": kv_bytes})
+        row = {"prefix": P, "comparator_ms": cm,
+               "comparator_GBps": c_bytes / (cm * 1e-3) / 1e9,
+               "hybrid_ms": hm,
+               "hybrid_GBps": step_bytes(B, H, L, d, F) / (hm * 1e-3) / 1e9,
+               "speedup": cm / hm, "comparator_kv_bytes": kv_bytes}
+        ns_auto = hba.prefix_softmax_auto_split(B, H, L, d, P)
+        if ns_auto > 1:
+            ws = torch.empty(hba.prefix_softmax_workspace_bytes(B, H, L, d, 64) // 4, device=dev)
+            sweep = {}
+            for ns in sorted({2, 4, 8, 16, 32, 64, ns_auto}):
+                sweep[ns] = _time_launches(torch, lambda: hba.prefix_softmax(
+                    q, k, v, Kc, Vc, out=out_c, n_split=ns, workspace=ws), 2, n, stream)
+            ref = hba.prefix_softmax(q, k, v, Kc, Vc, n_split=1)
+            hba.prefix_softmax(q, k, v, Kc, Vc, out=out_c, n_split=ns_auto, workspace=ws)
+            torch.cuda.synchronize()
+            err = float(((out_c - ref).norm(dim=-1) / ref.norm(dim=-1)).max())
+            sm = sweep[ns_auto]
+            row.update({"split_auto": ns_auto, "split_ms": sm,
+                        "split_GBps": c_bytes / (sm * 1e-3) / 1e9, "split_speedup_vs_hybrid": sm / hm,
+                        "split_sweep_ms": sweep, "split_vs_unsplit_max_row_rel": err})
+            del ws
+        rows.append(row)
         del Kc, Vc, S, Z
         torch.cuda.empty_cache()
     print(json.dumps({"mode": "comparator_sweep", "batch": B, "heads": H, "block": L, "head_dim": d,
@@ -267,6 +286,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--comparator", action="store_true",
                     help="time hba_prefix_softmax against hba_step at B=128 for P = 1k/4k/16k/32k")
+    ap.add_argument("--batch", default="128",
+                    help="comma-separated batch sizes for --comparator (e.g. 8,32,128)")
     ap.add_argument("--decode-loop", action="store_true",
                     help="time the B=32 decode loop (8 steps + 1 commit per 32-token block)")
     ap.add_argument("--blocks", type=int, default=256)
@@ -296,7 +317,9 @@ def main():
                           "launches": 10}), flush=True)
         return
     if args.comparator:
-        return comparator_sweep(args, torch, hba, wl, dev)
+        for B in (int(x) for x in args.batch.split(",")):
+            comparator_sweep(args, torch, hba, wl, dev, B)
+        return
     if args.decode_loop:
         return decode_loop(args, torch, hba, wl, dev)
     c = wl.serving_b128()

@@ -22,7 +22,8 @@ import torch
 from .pool import StatePool  # noqa: F401  (re-exported)
 
 __all__ = ["feature_map", "step", "commit", "prefix_softmax", "StatePool", "HbaError",
-           "library_path", "load_library", "abi_version", "step_commit"]
+           "library_path", "load_library", "abi_version", "step_commit", "prefix_softmax_workspace_bytes",
+           "prefix_softmax_auto_split"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libhba.so")
@@ -68,11 +69,17 @@ def load_library():
         lib.hba_abi_version.restype = ctypes.c_int32
         lib.hba_feature_map.argtypes = [sp, ctypes.c_int64, vp, vp, vp, vp]
         lib.hba_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        lib.hba_prefix_softmax_split.argtypes = [sp, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp]
+        lib.hba_prefix_softmax_auto_split.argtypes = [sp, i32]
+        lib.hba_prefix_softmax_auto_split.restype = i32
+        lib.hba_prefix_softmax_workspace_bytes.argtypes = [sp, i32]
+        lib.hba_prefix_softmax_workspace_bytes.restype = i64
         lib.hba_commit.argtypes = [sp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.hba_prefix_softmax.argtypes = [sp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.hba_step_commit.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         for fn in (lib.hba_feature_map, lib.hba_step, lib.hba_commit, lib.hba_prefix_softmax,
-                   lib.hba_step_commit):
+                   lib.hba_step_commit, lib.hba_prefix_softmax_split):
             fn.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -242,11 +249,16 @@ def commit(k, v, W, S_pool, Z_pool, n_valid=None, slot=None, stream=None):
           _p(S_pool), _p(Z_pool), _p(slot), _stream(stream))
 
 
-def prefix_softmax(q, k, v, Kc, Vc, prefix_len=None, out=None, stream=None):
+def prefix_softmax(q, k, v, Kc, Vc, prefix_len=None, out=None, stream=None, n_split=1, workspace=None):
     """Comparator: full softmax attention (section 2.2) of the block queries
     over [prefix cache ; block].  q [B][H][L][d]; k, v [B][Hkv][L][d];
     Kc, Vc [B][Hkv][P][d] (same dtype), Hkv dividing H; prefix_len [B] int32
-    or None (all P)."""
+    or None (all P).
+
+    n_split > 1 splits each (request, head)'s keys over that many workgroups
+    (hba_prefix_softmax_split); None takes the library's choice for the
+    current device.  The split needs a device workspace of
+    prefix_softmax_workspace_bytes(...) bytes, allocated here when not given."""
     lib = load_library()
     B, H, L, d = q.shape
     P = Kc.shape[2]
@@ -264,6 +276,36 @@ def prefix_softmax(q, k, v, Kc, Vc, prefix_len=None, out=None, stream=None):
     shape = Shape(B, H, L, d, 64, dt, 0, Hkv)
     kc = _p(Kc) if P > 0 else None
     vc = _p(Vc) if P > 0 else None
-    _call(lib.hba_prefix_softmax, "hba_prefix_softmax", ctypes.byref(shape), P, _p(prefix_len), _p(q),
-          _p(k), _p(v), kc, vc, _p(out), _stream(stream))
+    if n_split is None:
+        n_split = int(lib.hba_prefix_softmax_auto_split(ctypes.byref(shape), P))
+    if n_split == 1:
+        _call(lib.hba_prefix_softmax, "hba_prefix_softmax", ctypes.byref(shape), P, _p(prefix_len), _p(q),
+              _p(k), _p(v), kc, vc, _p(out), _stream(stream))
+        return out
+    need = int(lib.hba_prefix_softmax_workspace_bytes(ctypes.byref(shape), n_split))
+    if need < 0:
+        raise ValueError(f"n_split={n_split} is outside 1..64")
+    if workspace is None:
+        workspace = torch.empty((need + 3) // 4, device=q.device, dtype=torch.float32)
+    if workspace.dtype != torch.float32 or not workspace.is_contiguous() or workspace.numel() * 4 < need:
+        raise ValueError(f"workspace: need a contiguous fp32 tensor of at least {need} bytes")
+    _dev(workspace)
+    _call(lib.hba_prefix_softmax_split, "hba_prefix_softmax_split", ctypes.byref(shape), P, n_split,
+          _p(prefix_len), _p(q), _p(k), _p(v), kc, vc, _p(workspace), workspace.numel() * 4, _p(out),
+          _stream(stream))
     return out
+
+
+def prefix_softmax_workspace_bytes(B, H, L, d, n_split, dtype=torch.bfloat16) -> int:
+    """Workspace bytes of the split comparator (0 for n_split = 1)."""
+    shape = Shape(B, H, L, d, 64, _DTYPE[dtype], 0, 0)
+    need = int(load_library().hba_prefix_softmax_workspace_bytes(ctypes.byref(shape), n_split))
+    if need < 0:
+        raise ValueError("invalid shape or n_split")
+    return need
+
+
+def prefix_softmax_auto_split(B, H, L, d, max_prefix, dtype=torch.bfloat16) -> int:
+    """The library's key-split choice for the current device."""
+    shape = Shape(B, H, L, d, 64, _DTYPE[dtype], 0, 0)
+    return int(load_library().hba_prefix_softmax_auto_split(ctypes.byref(shape), max_prefix))

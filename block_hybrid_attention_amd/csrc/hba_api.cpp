@@ -6,7 +6,23 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "hba_internal.h"
+
+namespace hba {
+
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+        cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+}  // namespace hba
 
 namespace {
 
@@ -56,7 +72,7 @@ const char *hba_status_string(hba_status st) {
     return "unknown status";
 }
 
-int32_t hba_abi_version(void) { return 3; }
+int32_t hba_abi_version(void) { return 4; }
 
 hba_status hba_feature_map(const hba_shape *shape, int64_t n_rows, const void *x, const void *W,
                            float *phi, void *stream) {
@@ -131,17 +147,50 @@ hba_status hba_step_commit(const hba_shape *shape, const int32_t *n_valid, const
 hba_status hba_prefix_softmax(const hba_shape *shape, int32_t max_prefix, const int32_t *prefix_len,
                               const void *q, const void *k, const void *v, const void *Kc,
                               const void *Vc, float *out, void *stream) {
+    return hba_prefix_softmax_split(shape, max_prefix, 1, prefix_len, q, k, v, Kc, Vc, nullptr, 0, out, stream);
+}
+
+int32_t hba_prefix_softmax_auto_split(const hba_shape *shape, int32_t max_prefix) {
+    if (check_common(shape, true, false) != HBA_OK || max_prefix < 0) return 1;
+    // one workgroup per compute unit is resident at a time, so aim for one
+    // round of workgroups over the device, with at least 256 keys per split
+    const int64_t pairs = (int64_t)shape->batch * shape->heads;
+    const int cus = hba::device_cus();
+    if (pairs <= 0 || cus <= 0) return 1;
+    const int64_t want = ((int64_t)cus + pairs - 1) / pairs;
+    const int64_t by_len = ((int64_t)max_prefix + shape->block) / 256;
+    int64_t ns = want < by_len ? want : by_len;
+    if (ns > hba::kMaxPrefixSplit) ns = hba::kMaxPrefixSplit;
+    return ns < 1 ? 1 : (int32_t)ns;
+}
+
+int64_t hba_prefix_softmax_workspace_bytes(const hba_shape *shape, int32_t n_split) {
+    if (check_common(shape, true, false) != HBA_OK || n_split < 1 || n_split > hba::kMaxPrefixSplit) return -1;
+    if (n_split == 1) return 0;
+    return 4 * (int64_t)shape->batch * shape->heads * n_split * shape->block * (shape->head_dim + 2);
+}
+
+hba_status hba_prefix_softmax_split(const hba_shape *shape, int32_t max_prefix, int32_t n_split,
+                                    const int32_t *prefix_len, const void *q, const void *k, const void *v,
+                                    const void *Kc, const void *Vc, float *workspace, int64_t workspace_bytes,
+                                    float *out, void *stream) {
     hba_status st = check_common(shape, true, false);
     if (st != HBA_OK) return st;
     const int G = kv_group(shape);
     if (max_prefix < 0 || (int64_t)max_prefix + shape->block > 0x7fffffff || G == 0) return HBA_ERR_SHAPE;
+    if (n_split < 1 || n_split > hba::kMaxPrefixSplit) return HBA_ERR_SHAPE;
+    if ((int64_t)shape->batch * shape->heads * n_split > kMaxGrid) return HBA_ERR_SHAPE;
     if (shape->batch == 0) return HBA_OK;
     if (!q || !k || !v || !out) return HBA_ERR_NULL;
     if (max_prefix > 0 && (!Kc || !Vc)) return HBA_ERR_NULL;
+    if (n_split > 1 && !workspace) return HBA_ERR_NULL;
+    if (n_split > 1 && workspace_bytes < hba_prefix_softmax_workspace_bytes(shape, n_split)) return HBA_ERR_CAPACITY;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
-        (max_prefix > 0 && (!aligned16(Kc) || !aligned16(Vc))) || (prefix_len && !aligned4(prefix_len)))
+        (max_prefix > 0 && (!aligned16(Kc) || !aligned16(Vc))) || (prefix_len && !aligned4(prefix_len)) ||
+        (n_split > 1 && !aligned16(workspace)))
         return HBA_ERR_ALIGN;
-    hba::PrefixArgs a{prefix_len, q, k, v, Kc, Vc, out, shape->batch, shape->heads, shape->block, max_prefix, G};
+    hba::PrefixArgs a{prefix_len, q, k, v, Kc, Vc, out, shape->batch, shape->heads, shape->block, max_prefix, G,
+                      n_split > 1 ? workspace : nullptr, n_split};
     return from_hip(hba::launch_prefix_softmax(a, shape->in_dtype == HBA_BF16, shape->head_dim,
                                                static_cast<hipStream_t>(stream)));
 }

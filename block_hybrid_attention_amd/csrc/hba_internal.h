@@ -64,7 +64,19 @@ struct PrefixArgs {
     float *out;                 // [B][H][L][d]
     int B, H, L, P;
     int G;
+    // Split over keys: NS workgroups per (request, head), split s taking a
+    // contiguous run of key tiles.  NS == 1 writes out directly; NS > 1
+    // writes normalised partial outputs [B*H][NS][L][d] followed by the
+    // partial (max, sum) pairs [B*H][NS][2][L] to part, merged afterwards.
+    float *part;
+    int NS;
 };
+
+// Largest key split of the comparator.
+constexpr int kMaxPrefixSplit = 64;
+
+// Compute units of the current device (0 if the runtime cannot say).
+int device_cus();
 
 // Enqueue kernel `k` with a single by-value argument block on `stream`; the
 // returned status is this launch's own.

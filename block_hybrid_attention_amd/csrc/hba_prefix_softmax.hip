@@ -16,6 +16,12 @@
 //   bf16 inputs: 32-key tiles, both products on bf16 MFMA (P split into a
 //   high part and a residual, V exact), V staged transposed in LDS.
 // The next tile's K and V are loaded before the current one is computed.
+//
+// Few (request, head) pairs (small batches) leave most compute units idle,
+// so the keys can also be split: NS workgroups per pair each take a
+// contiguous run of key tiles and write a normalised partial output with its
+// running max and sum; prefix_combine_kernel then merges the NS partials of
+// each query with the usual rescaling (the same algebra that merges waves).
 #include "hba_device.h"
 #include "hba_internal.h"
 
@@ -100,7 +106,66 @@ __device__ __forceinline__ void v_row_f32(const PrefixOps<T, D> &op, int r, floa
     }
 }
 
-template <typename T, int D>
+// Key-tile range [tb, te) of split sp out of ns for a pair with ntiles tiles.
+__device__ __forceinline__ void split_range(int ntiles, int ns, int sp, int &tb, int &te) {
+    const int per = (ntiles + ns - 1) / ns;
+    tb = min(sp * per, ntiles);
+    te = min(tb + per, ntiles);
+}
+
+// Epilogue shared by the comparator kernels: obuf holds each wave's output
+// rows already scaled to the workgroup's common max and divided by its sum
+// (row stride OLD floats); add the four waves and store.  Unsplit: the
+// result is the output.  Split: it is the split's partial output, stored
+// with the split's max M and sum Lt per query (both zero-weight, M = -inf,
+// Lt = 0, when the split holds no keys).
+template <int D, int OLD, bool SPLIT>
+__device__ __forceinline__ void prefix_store(const PrefixArgs &a, int64_t bh, int sp, const float *obuf,
+                                             const float (*mbuf)[kRows], const float (*lbuf)[kRows], int tid) {
+    const int L = a.L;
+    float *og;
+    if constexpr (SPLIT) {
+        const int64_t p = bh * a.NS + sp;
+        og = a.part + p * L * D;
+        if (tid < L) {
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) M = fmaxf(M, mbuf[w][tid]);
+            float Lt = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                Lt += lbuf[w][tid] > 0.f ? lbuf[w][tid] * __builtin_amdgcn_exp2f(mbuf[w][tid] - M) : 0.f;
+            float *ml = a.part + (int64_t)a.B * a.H * a.NS * L * D + p * 2 * L;
+            ml[tid] = M;
+            ml[L + tid] = Lt;
+        }
+    } else {
+        og = a.out + bh * L * D;
+    }
+#pragma unroll
+    for (int it = 0; it < kRows * D / 4 / kThreads; ++it) {
+        const int e = tid + it * kThreads;
+        const int qi = e / (D / 4), c = 4 * (e % (D / 4));
+        if (qi < L) {
+            floatx4 v = *reinterpret_cast<const floatx4 *>(obuf + (0 * kRows + qi) * OLD + c);
+#pragma unroll
+            for (int w = 1; w < 4; ++w) v += *reinterpret_cast<const floatx4 *>(obuf + (w * kRows + qi) * OLD + c);
+            if constexpr (SPLIT)
+                *reinterpret_cast<floatx4 *>(og + (int64_t)qi * D + c) = v;
+            else
+                __builtin_nontemporal_store(v, reinterpret_cast<floatx4 *>(og + (int64_t)qi * D + c));
+        }
+    }
+}
+
+// Scale that brings one wave's rows to the workgroup's common max M and
+// divides by the workgroup's sum Lt; a split with no keys has Lt = 0 and
+// contributes zeros.
+__device__ __forceinline__ float wave_scale(float m, float M, float Lt) {
+    return Lt > 0.f ? __builtin_amdgcn_exp2f(m - M) / Lt : 0.f;
+}
+
+template <typename T, int D, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void prefix_kernel(PrefixArgs a) {
     using O = PrefixOps<T, D>;
     constexpr int NCT = O::NCT;
@@ -112,7 +177,8 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(PrefixArgs a) {
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int64_t bh = blockIdx.x;
+    const int64_t bh = SPLIT ? (int64_t)blockIdx.x / a.NS : (int64_t)blockIdx.x;
+    const int sp = SPLIT ? (int)((int64_t)blockIdx.x - bh * a.NS) : 0;
     const int64_t kvh = bh / a.G;
     const int b = (int)(bh / a.H);
     const int L = a.L;
@@ -120,6 +186,8 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(PrefixArgs a) {
     P = P < 0 ? 0 : (P > a.P ? a.P : P);
     const int nkeys = P + L;
     const int ntiles = (nkeys + 15) / 16;
+    int tb = 0, te = ntiles;
+    if constexpr (SPLIT) split_range(ntiles, a.NS, sp, tb, te);
 
     // queries as the B operand of S^T = K Q^T: lane holds query 16 nt + li
     const T *qg = static_cast<const T *>(a.q) + bh * L * D;
@@ -147,12 +215,12 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(PrefixArgs a) {
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
     PrefixOps<T, D> cur, nxt;
-    if (wave < ntiles) load_tile<T, D>(a, kvh, P, nkeys, 16 * wave, li, lg, cur);
+    if (tb + wave < te) load_tile<T, D>(a, kvh, P, nkeys, 16 * (tb + wave), li, lg, cur);
 #pragma unroll 1
-    for (int tile = wave; tile < ntiles; tile += 4) {
+    for (int tile = tb + wave; tile < te; tile += 4) {
         const int j0 = 16 * tile;
         {   // prefetch the wave's next tile (clamped to the last one)
-            const int tn = tile + 4 < ntiles ? tile + 4 : ntiles - 1;
+            const int tn = tile + 4 < te ? tile + 4 : te - 1;
             load_tile<T, D>(a, kvh, P, nkeys, 16 * tn, li, lg, nxt);
         }
         floatx4 s[2];
@@ -225,8 +293,9 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(PrefixArgs a) {
         for (int w = 0; w < 4; ++w) M = fmaxf(M, mbuf[w][qi]);
         float Lt = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) Lt += lbuf[w][qi] * __builtin_amdgcn_exp2f(mbuf[w][qi] - M);
-        const float sc = __builtin_amdgcn_exp2f(m[nt] - M) / Lt;
+        for (int w = 0; w < 4; ++w)
+            Lt += lbuf[w][qi] > 0.f ? lbuf[w][qi] * __builtin_amdgcn_exp2f(mbuf[w][qi] - M) : 0.f;
+        const float sc = wave_scale(m[nt], M, Lt);
 #pragma unroll
         for (int c = 0; c < NCT; ++c)
 #pragma unroll
@@ -234,17 +303,7 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(PrefixArgs a) {
                 obuf[(wave * kRows + qi) * OLD + NCT * (4 * lg + r) + c] = o[c][nt][r] * sc;
     }
     __syncthreads();
-    float *og = a.out + bh * L * D;
-#pragma unroll
-    for (int it = 0; it < kRows * D / kThreads; ++it) {
-        const int e = tid + it * kThreads;
-        const int qi = e / D, c = e % D;
-        if (qi < L) {
-            const float v = obuf[(0 * kRows + qi) * OLD + c] + obuf[(1 * kRows + qi) * OLD + c] +
-                            obuf[(2 * kRows + qi) * OLD + c] + obuf[(3 * kRows + qi) * OLD + c];
-            og[(int64_t)qi * D + c] = v;
-        }
-    }
+    prefix_store<D, OLD, SPLIT>(a, bh, sp, obuf, mbuf, lbuf, tid);
 }
 
 // bf16 inputs: both products on bf16 MFMA.  Waves take interleaved 32-key
@@ -265,7 +324,7 @@ struct PrefixGeomBf16 {
     static constexpr int bytes = (4 * vt_bytes > ob_bytes ? 4 * vt_bytes : ob_bytes);
 };
 
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void prefix_kernel_bf16(PrefixArgs a) {
     using T = uint16_t;
     using G = PrefixGeomBf16<D>;
@@ -278,7 +337,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel_bf16(PrefixArgs a) 
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int64_t bh = blockIdx.x;
+    const int64_t bh = SPLIT ? (int64_t)blockIdx.x / a.NS : (int64_t)blockIdx.x;
+    const int sp = SPLIT ? (int)((int64_t)blockIdx.x - bh * a.NS) : 0;
     const int64_t kvh = bh / a.G;
     const int b = (int)(bh / a.H);
     const int L = a.L;
@@ -286,6 +346,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel_bf16(PrefixArgs a) 
     P = P < 0 ? 0 : (P > a.P ? a.P : P);
     const int nkeys = P + L;
     const int ntiles = (nkeys + 31) / 32;
+    int tb = 0, te = ntiles;
+    if constexpr (SPLIT) split_range(ntiles, a.NS, sp, tb, te);
+    const int nt_ = te - tb;   // this workgroup's tiles: tb, tb + 1, ...
     T *vt = reinterpret_cast<T *>(smem + wave * G::vt_bytes);
 
     // queries as the B operand of S^T = K Q^T: lane holds query 16 nt + li
@@ -404,14 +467,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel_bf16(PrefixArgs a) 
     // two tiles in flight per wave, ping-ponged without copies (a register
     // copy of the prefetched tile would wait for all of its loads)
     Tile t0, t1;
-    if (wave < ntiles) load(32 * wave, t0);
+    if (wave < nt_) load(32 * (tb + wave), t0);
 #pragma unroll 1
-    for (int tile = wave; tile < ntiles; tile += 8) {
-        load(32 * (tile + 4 < ntiles ? tile + 4 : ntiles - 1), t1);
-        process(tile, t0);
-        if (tile + 4 >= ntiles) break;
-        load(32 * (tile + 8 < ntiles ? tile + 8 : ntiles - 1), t0);
-        process(tile + 4, t1);
+    for (int i = wave; i < nt_; i += 8) {
+        load(32 * (tb + (i + 4 < nt_ ? i + 4 : nt_ - 1)), t1);
+        process(tb + i, t0);
+        if (i + 4 >= nt_) break;
+        load(32 * (tb + (i + 8 < nt_ ? i + 8 : nt_ - 1)), t0);
+        process(tb + i + 4, t1);
     }
 
     // merge the four waves' partial softmax states (the V^T tiles are dead)
@@ -431,34 +494,76 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel_bf16(PrefixArgs a) 
         for (int w = 0; w < 4; ++w) M = fmaxf(M, mbuf[w][qi]);
         float Lt = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) Lt += lbuf[w][qi] * __builtin_amdgcn_exp2f(mbuf[w][qi] - M);
-        const float sc_ = __builtin_amdgcn_exp2f(m[nt] - M) / Lt;
+        for (int w = 0; w < 4; ++w)
+            Lt += lbuf[w][qi] > 0.f ? lbuf[w][qi] * __builtin_amdgcn_exp2f(mbuf[w][qi] - M) : 0.f;
+        const float sc_ = wave_scale(m[nt], M, Lt);
 #pragma unroll
         for (int c = 0; c < NCT; ++c)
             *reinterpret_cast<float4 *>(obuf + (wave * kRows + qi) * G::OLD + 16 * c + 4 * lg) =
                 make_float4(o[c][nt][0] * sc_, o[c][nt][1] * sc_, o[c][nt][2] * sc_, o[c][nt][3] * sc_);
     }
     __syncthreads();
-    float *og = a.out + bh * L * D;
-#pragma unroll
-    for (int it = 0; it < kRows * D / 4 / kThreads; ++it) {
-        const int e = tid + it * kThreads;
-        const int qi = e / (D / 4), c = 4 * (e % (D / 4));
-        if (qi < L) {
-            floatx4 v = *reinterpret_cast<const floatx4 *>(obuf + (0 * kRows + qi) * G::OLD + c);
-#pragma unroll
-            for (int w = 1; w < 4; ++w) v += *reinterpret_cast<const floatx4 *>(obuf + (w * kRows + qi) * G::OLD + c);
-            __builtin_nontemporal_store(v, reinterpret_cast<floatx4 *>(og + (int64_t)qi * D + c));
+    prefix_store<D, G::OLD, SPLIT>(a, bh, sp, obuf, mbuf, lbuf, tid);
+}
+
+// Merge of the NS key splits of each (request, head): with split maxima
+// M_s and sums Lt_s, query i's output is
+//   sum_s Lt_s 2^(M_s - M) o_s / sum_s Lt_s 2^(M_s - M),   M = max_s M_s,
+// where o_s is split s's normalised partial output.  Grid: (pair, slice of
+// kThreads output float4s); the NS partial loads of a float4 are unrolled so
+// they are in flight together.
+template <int D>
+__global__ __launch_bounds__(kThreads) void prefix_combine_kernel(PrefixArgs a) {
+    __shared__ float wgt[kMaxPrefixSplit][kRows];
+    const int tid = (int)threadIdx.x;
+    const int64_t bh = blockIdx.x;
+    const int L = a.L, NS = a.NS;
+    const float *po = a.part + bh * NS * L * D;
+    const float *ml = a.part + (int64_t)a.B * a.H * NS * L * D + bh * NS * 2 * L;
+    if (tid < L) {
+        float M = -INFINITY;
+        for (int s_ = 0; s_ < NS; ++s_) M = fmaxf(M, ml[s_ * 2 * L + tid]);
+        float den = 0.f;
+        for (int s_ = 0; s_ < NS; ++s_) {
+            const float lt = ml[s_ * 2 * L + L + tid];
+            const float w = lt > 0.f ? lt * __builtin_amdgcn_exp2f(ml[s_ * 2 * L + tid] - M) : 0.f;
+            wgt[s_][tid] = w;
+            den += w;
         }
+        const float inv = 1.f / den;   // den > 0: every query sees at least its block's keys
+        for (int s_ = 0; s_ < NS; ++s_) wgt[s_][tid] *= inv;
+    }
+    __syncthreads();
+    float *og = a.out + bh * L * D;
+    const int e = (int)blockIdx.y * kThreads + tid;
+    if (e < L * D / 4) {
+        const int qi = e / (D / 4), c = 4 * (e % (D / 4));
+        floatx4 v = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int s_ = 0; s_ < NS; ++s_)
+            v += wgt[s_][qi] * *reinterpret_cast<const floatx4 *>(po + ((int64_t)s_ * L + qi) * D + c);
+        __builtin_nontemporal_store(v, reinterpret_cast<floatx4 *>(og + (int64_t)qi * D + c));
     }
 }
 
 template <typename T, int D>
 static hipError_t launch_prefix_t(const PrefixArgs &a, hipStream_t stream) {
+    const unsigned pairs = (unsigned)(a.B * a.H);
+    if (a.NS <= 1) {
+        if constexpr (sizeof(T) == 2)
+            return launch_kernel(prefix_kernel_bf16<D, false>, dim3(pairs), dim3(kThreads), a, stream);
+        else
+            return launch_kernel(prefix_kernel<T, D, false>, dim3(pairs), dim3(kThreads), a, stream);
+    }
+    const dim3 grid((unsigned)((int64_t)pairs * a.NS));
+    hipError_t e;
     if constexpr (sizeof(T) == 2)
-        return launch_kernel(prefix_kernel_bf16<D>, dim3((unsigned)(a.B * a.H)), dim3(kThreads), a, stream);
+        e = launch_kernel(prefix_kernel_bf16<D, true>, grid, dim3(kThreads), a, stream);
     else
-        return launch_kernel(prefix_kernel<T, D>, dim3((unsigned)(a.B * a.H)), dim3(kThreads), a, stream);
+        e = launch_kernel(prefix_kernel<T, D, true>, grid, dim3(kThreads), a, stream);
+    if (e != hipSuccess) return e;
+    const unsigned slices = (unsigned)((a.L * D / 4 + kThreads - 1) / kThreads);
+    return launch_kernel(prefix_combine_kernel<D>, dim3(pairs, slices), dim3(kThreads), a, stream);
 }
 
 hipError_t launch_prefix_softmax(const PrefixArgs &a, bool bf16, int d, hipStream_t stream) {

@@ -671,17 +671,6 @@ __global__ __launch_bounds__(kThreads, 3) void step_kernel_bf16(StepArgs a) {
 }
 
 // compute units of the current device (cached per device; 0 if unknown)
-static int device_cus() {
-    static int cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cache[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cache[dev] = n;
-    }
-    return cache[dev];
-}
-
 template <typename T, int D, int F>
 static hipError_t launch_step_t(const StepArgs &a, hipStream_t stream) {
     if constexpr (sizeof(T) == 2) {

@@ -181,11 +181,47 @@ hba_status hba_prefix_softmax(const hba_shape *shape, int32_t max_prefix,
                               const void *v, const void *Kc, const void *Vc, float *out,
                               void *stream);
 
+/* The comparator with its keys split over several workgroups per (request,
+ * head), for batches too small to fill the GPU with one workgroup per pair
+ * (the small-batch columns of Appendix A, Table 3).  Same result as
+ * hba_prefix_softmax up to rounding: split s of a pair takes a contiguous
+ * run of its P + L keys, writes its softmax-normalised partial output with
+ * its running max and sum to the workspace, and a second kernel merges the
+ * n_split partials of each query by rescaling them to their common max.
+ * Reads: as hba_prefix_softmax.
+ *   n_split          1..64 key splits per pair; 1 runs hba_prefix_softmax and
+ *                    ignores the workspace.  hba_prefix_softmax_auto_split
+ *                    gives a choice for the current device.
+ *   workspace        device scratch of workspace_bytes >= the value of
+ *                    hba_prefix_softmax_workspace_bytes(shape, n_split)
+ *                    (4 B H n_split L (d + 2) bytes), 16-byte aligned, owned
+ *                    by the caller; its contents on entry do not matter and
+ *                    are undefined on return.  Calls in flight at the same
+ *                    time need separate workspaces.
+ *   other arguments  as hba_prefix_softmax.
+ * Errors: as hba_prefix_softmax; HBA_ERR_SHAPE for n_split outside 1..64,
+ * HBA_ERR_NULL for a NULL workspace with n_split > 1, HBA_ERR_CAPACITY for
+ * a workspace smaller than required. */
+hba_status hba_prefix_softmax_split(const hba_shape *shape, int32_t max_prefix, int32_t n_split,
+                                    const int32_t *prefix_len, const void *q, const void *k,
+                                    const void *v, const void *Kc, const void *Vc, float *workspace,
+                                    int64_t workspace_bytes, float *out, void *stream);
+
+/* Key splits for hba_prefix_softmax_split on the current device: enough
+ * workgroups for one per compute unit, at least 256 keys per split, at most
+ * 64; 1 when one workgroup per pair already fills the device or the shape is
+ * invalid.  Reads: batch, heads, block, head_dim, in_dtype. */
+int32_t hba_prefix_softmax_auto_split(const hba_shape *shape, int32_t max_prefix);
+
+/* Workspace bytes hba_prefix_softmax_split needs: 0 for n_split = 1,
+ * 4 B H n_split L (d + 2) otherwise, -1 for an invalid shape or n_split. */
+int64_t hba_prefix_softmax_workspace_bytes(const hba_shape *shape, int32_t n_split);
+
 /* Static description of a status code (never NULL). */
 const char *hba_status_string(hba_status status);
 
-/* Library ABI version, currently 3 (2 added hba_step_commit, 3 added
- * hba_shape.kv_heads). */
+/* Library ABI version, currently 4 (2 added hba_step_commit, 3 added
+ * hba_shape.kv_heads, 4 added the split comparator). */
 int32_t hba_abi_version(void);
 
 #ifdef __cplusplus

@@ -31,17 +31,18 @@ def lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:hba_status|const char \*|int32_t)\s*\**\s*(hba_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:hba_status|const char \*|int32_t|int64_t)\s*\**\s*(hba_\w+)\s*\(", text, re.M)))
 
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"hba_feature_map", "hba_step", "hba_commit", "hba_prefix_softmax", "hba_step_commit",
+            "hba_prefix_softmax_split", "hba_prefix_softmax_auto_split", "hba_prefix_softmax_workspace_bytes",
             "hba_status_string", "hba_abi_version"} <= set(names)
     L = lib()
     for n in names:
         assert hasattr(L, n), n
-    assert hba.abi_version() == 3
+    assert hba.abi_version() == 4
 
 
 def test_status_strings():
@@ -172,6 +173,32 @@ def test_python_binding_refuses_uneven_head_groups():
     k = torch.zeros(1, 3, 8, 64)
     with pytest.raises(ValueError, match="key/value heads"):
         hba.step(q, k, k, torch.zeros(4, 64, 64), torch.zeros(1, 4, 128, 64), torch.zeros(1, 4, 128))
+
+
+@no_gpu_only
+def test_split_comparator_validation():
+    L = lib()
+
+    def call(sh, P=128, ns=4, ws=A2, wsb=1 << 30, Kc=A, out=A2):
+        return L.hba_prefix_softmax_split(ctypes.byref(sh), P, ns, None, A, A, A, Kc, A, ws, wsb, out, None)
+
+    sh = shape()
+    need = L.hba_prefix_softmax_workspace_bytes(ctypes.byref(sh), 4)
+    assert need == 4 * 2 * 4 * 4 * 32 * (128 + 2)
+    assert L.hba_prefix_softmax_workspace_bytes(ctypes.byref(sh), 1) == 0
+    assert L.hba_prefix_softmax_workspace_bytes(ctypes.byref(sh), 0) == -1
+    assert L.hba_prefix_softmax_workspace_bytes(ctypes.byref(sh), 65) == -1
+    assert call(sh, ns=0) == ESHAPE
+    assert call(sh, ns=65) == ESHAPE
+    assert call(sh, ws=None) == ENULL
+    assert call(sh, wsb=need - 1) == ECAP
+    assert call(sh, ws=MIS) == EALIGN
+    assert call(sh, Kc=None) == ENULL
+    assert call(shape(kv_heads=3)) == ESHAPE
+    assert call(shape(batch=0), ws=None) == OK
+    # without a device the choice falls back to one split; bad shapes give 1 too
+    assert L.hba_prefix_softmax_auto_split(ctypes.byref(sh), 1 << 15) == 1
+    assert L.hba_prefix_softmax_auto_split(None, 128) == 1
 
 
 def test_python_binding_refuses_host_tensors():
