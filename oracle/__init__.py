@@ -60,7 +60,9 @@ def _lib():
                                  _f64p, _f64p, _i32p, _f64p, ctypes.c_int]
         lib.orc_prefix_softmax.argtypes = [i32, i32, i32, i32, i32, i32, _i32p, _f64p, _f64p, _f64p,
                                            _f64p, _f64p, _f64p, ctypes.c_int]
-        for fn in (lib.orc_feature_map, lib.orc_commit, lib.orc_step, lib.orc_prefix_softmax):
+        lib.orc_transfer.argtypes = [i32, i32, i32, i32, i32, i32, i32, _f64p, _f64p, _f64p, _f64p, _f64p,
+                                     _f64p, _f64p, _f64p, _f64p, _f64p, ctypes.c_int]
+        for fn in (lib.orc_feature_map, lib.orc_commit, lib.orc_step, lib.orc_prefix_softmax, lib.orc_transfer):
             fn.restype = ctypes.c_int
         _lib_handle = lib
     return _lib_handle
@@ -166,3 +168,30 @@ def prefix_softmax(q, k, v, Kc, Vc, prefix_len=None, nthreads: int = 0) -> np.nd
     if rc:
         raise OracleError(f"orc_prefix_softmax rc={rc}")
     return out
+
+
+def transfer(q, k, v, W, alpha, target, block: int, nthreads: int = 0):
+    """Stage-1 attention transfer (section 3.2) for one layer: the hybrid
+    output over whole sequences of N = n_blocks * block tokens (section 3.1:
+    block softmax plus the states of all earlier blocks), the summed squared
+    error against ``target`` and its gradient with respect to W and alpha.
+    q, target [B][H][N][d]; k, v [B][Hkv][N][d]; W [H][d][F]; alpha [H].
+    Returns (out, loss, dW, dalpha)."""
+    q, k, v, W = _f64(q), _f64(k), _f64(v), _f64(W)
+    alpha, target = _f64(alpha), _f64(target)
+    B, H, N, d = q.shape
+    F = W.shape[2]
+    Hkv = _kv_heads(H, k.shape[1])
+    if N % block:
+        raise OracleError(f"{N} tokens are not whole blocks of {block}")
+    assert k.shape == (B, Hkv, N, d) and v.shape == k.shape and target.shape == q.shape
+    assert W.shape == (H, d, F) and alpha.shape == (H,)
+    out = np.zeros((B, H, N, d))
+    loss = np.zeros(1)
+    dW = np.zeros((H, d, F))
+    dalpha = np.zeros(H)
+    rc = _lib().orc_transfer(B, H, Hkv, N // block, block, d, F, _p(q), _p(k), _p(v), _p(W), _p(alpha),
+                             _p(target), _p(out), _p(loss), _p(dW), _p(dalpha), nthreads)
+    if rc:
+        raise OracleError(f"orc_transfer rc={rc}")
+    return out, float(loss[0]), dW, dalpha

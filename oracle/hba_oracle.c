@@ -264,3 +264,179 @@ int orc_prefix_softmax(int B, int H, int Hkv, int L, int d, int max_prefix,
     }
     return bad ? 3 : 0;
 }
+
+/* Stage-1 attention transfer (section 3.2): the layer's hybrid output over a
+ * whole training sequence of N = n_blocks * L tokens, its squared error
+ * against the softmax teacher's output, and the gradient of that error with
+ * respect to the layer's own parameters W and alpha (the backbone, hence q,
+ * k, v and the teacher, is frozen).
+ *
+ * Forward (section 3.1 over the sequence): the queries of block n use exact
+ * softmax over block n, the states S_{n-1}, Z_{n-1} of blocks 0..n-1, and
+ *   o_i = (w sm_num_i + phi(q_i)^T S_{n-1}) / (w sm_den_i + phi(q_i)^T Z_{n-1}),
+ * w = sigma(alpha[h]).  Loss: L = sum over b, h, i, c of (o_ic - target_ic)^2,
+ * the squared L2 norm of the section 3.2 objective for one layer and batch.
+ *
+ * Backward, by the chain rule, with g_i = dL/do_i = 2 (o_i - t_i):
+ *   dL/dnum_i = g_i / den_i,   dL/dden_i = -(g_i . o_i) / den_i
+ *   dL/dw     = sum_i dL/dnum_i . sm_num_i + dL/dden_i sm_den_i,
+ *   dL/dalpha = dL/dw * w (1 - w)
+ *   dL/dphi(q_i) = S_{n-1} dL/dnum_i + Z_{n-1} dL/dden_i
+ *   dL/dphi(k_t) (t in block m) = G_m v_t + Gz_m, where G_m and Gz_m sum
+ *       phi(q_i) dL/dnum_i^T and phi(q_i) dL/dden_i over the queries i of
+ *       all blocks after m (those whose states contain k_t)
+ *   phi = [p, p'] with p = softmax(u), p' = softmax(-u), u = x W:
+ *   dL/du_f = p_f (dp_f - p . dp) - p'_f (dp'_f - p' . dp')
+ *   dL/dW  += x dL/du^T for every query row x = q_i and key row x = k_t.
+ * Layouts: q, target, out [B][H][N][d]; k, v [B][Hkv][N][d]; W, dW
+ * [H][d][F]; alpha, dalpha [H]; out may be NULL.  dW, dalpha and loss are
+ * overwritten.  The per-(request, head) parts are summed over requests in
+ * request order. */
+static void phi_backward(int F, const double *phi, const double *dphi, double *du) {
+    double sp = 0.0, sn = 0.0;
+    for (int f = 0; f < F; ++f) {
+        sp += phi[f] * dphi[f];
+        sn += phi[F + f] * dphi[F + f];
+    }
+    for (int f = 0; f < F; ++f)
+        du[f] = phi[f] * (dphi[f] - sp) - phi[F + f] * (dphi[F + f] - sn);
+}
+
+int orc_transfer(int B, int H, int Hkv, int n_blocks, int L, int d, int F,
+                 const double *q, const double *k, const double *v,
+                 const double *W, const double *alpha, const double *target,
+                 double *out, double *loss, double *dW, double *dalpha,
+                 int nthreads) {
+    if (B < 0 || H <= 0 || Hkv <= 0 || H % Hkv || n_blocks < 0 || L <= 0 || d <= 0 || F <= 0) return 1;
+    const int P2 = 2 * F;
+    const int64_t N = (int64_t)n_blocks * L;
+    const double scale = 1.0 / sqrt((double)d);
+    const int64_t nbh = (int64_t)B * H;
+    /* per-(request, head) parts, summed in request order at the end */
+    double *pW = (double *)calloc((size_t)(nbh > 0 ? nbh : 1) * d * F, sizeof(double));
+    double *pw = (double *)calloc((size_t)(nbh > 0 ? nbh : 1), sizeof(double));
+    double *pl = (double *)calloc((size_t)(nbh > 0 ? nbh : 1), sizeof(double));
+    int nt = threads_or_default(nthreads);
+    int bad = 0;
+    #pragma omp parallel for num_threads(nt) schedule(dynamic) reduction(|:bad)
+    for (int64_t bh = 0; bh < nbh; ++bh) {
+        int b = (int)(bh / H), h = (int)(bh % H);
+        const int64_t kvh = kv_index(b, h, H, Hkv);
+        const double *Wh = W + (int64_t)h * d * F;
+        const double w = 1.0 / (1.0 + exp(-alpha[h]));
+        const double *qb = q + bh * N * d, *tb = target + bh * N * d;
+        const double *kb = k + kvh * N * d, *vb = v + kvh * N * d;
+        double *S = (double *)calloc((size_t)P2 * d, sizeof(double));
+        double *Z = (double *)calloc((size_t)P2, sizeof(double));
+        double *phq = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1) * P2);
+        double *dnum = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1) * d);
+        double *dden = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double *u = (double *)malloc(sizeof(double) * F);
+        double *p = (double *)malloc(sizeof(double) * P2);
+        double *dp = (double *)malloc(sizeof(double) * P2);
+        double *du = (double *)malloc(sizeof(double) * F);
+        double *smn = (double *)malloc(sizeof(double) * d);
+        double *o = (double *)malloc(sizeof(double) * d);
+        double *gW = pW + bh * d * F;
+        for (int n = 0; n < n_blocks; ++n) {
+            const int64_t i0 = (int64_t)n * L;
+            for (int64_t i = i0; i < i0 + L; ++i) {
+                const double *qi = qb + i * d;
+                /* within-block softmax branch */
+                double smd = 0.0;
+                for (int c = 0; c < d; ++c) smn[c] = 0.0;
+                for (int64_t j = i0; j < i0 + L; ++j) {
+                    double sc = 0.0;
+                    for (int c = 0; c < d; ++c) sc += qi[c] * kb[j * d + c];
+                    sc *= scale;
+                    if (!(fabs(sc) <= ORC_MAX_ABS_SCORE)) bad |= 4;
+                    double a = exp(sc);
+                    smd += a;
+                    for (int c = 0; c < d; ++c) smn[c] += a * vb[j * d + c];
+                }
+                /* linear readout of blocks 0..n-1 and the shared normaliser */
+                double *ph = phq + i * P2;
+                phi_row(d, F, qi, Wh, u, ph);
+                double den = w * smd;
+                for (int f = 0; f < P2; ++f) den += ph[f] * Z[f];
+                for (int c = 0; c < d; ++c) {
+                    double lin = 0.0;
+                    for (int f = 0; f < P2; ++f) lin += ph[f] * S[(int64_t)f * d + c];
+                    o[c] = (w * smn[c] + lin) / den;
+                }
+                if (out)
+                    for (int c = 0; c < d; ++c) out[(bh * N + i) * d + c] = o[c];
+                /* loss and the gradient at the merge */
+                double go = 0.0;
+                for (int c = 0; c < d; ++c) {
+                    const double e = o[c] - tb[i * d + c];
+                    pl[bh] += e * e;
+                    go += 2.0 * e * o[c];
+                }
+                dden[i] = -go / den;
+                for (int c = 0; c < d; ++c) dnum[i * d + c] = 2.0 * (o[c] - tb[i * d + c]) / den;
+                double gw = dden[i] * smd;
+                for (int c = 0; c < d; ++c) gw += dnum[i * d + c] * smn[c];
+                pw[bh] += gw;
+                /* through phi(q_i) into W */
+                for (int f = 0; f < P2; ++f) {
+                    double acc = Z[f] * dden[i];
+                    for (int c = 0; c < d; ++c) acc += S[(int64_t)f * d + c] * dnum[i * d + c];
+                    dp[f] = acc;
+                }
+                phi_backward(F, ph, dp, du);
+                for (int r = 0; r < d; ++r)
+                    for (int f = 0; f < F; ++f) gW[(int64_t)r * F + f] += qi[r] * du[f];
+            }
+            /* commit block n */
+            for (int64_t t = i0; t < i0 + L; ++t) {
+                phi_row(d, F, kb + t * d, Wh, u, p);
+                for (int f = 0; f < P2; ++f) {
+                    Z[f] += p[f];
+                    for (int c = 0; c < d; ++c) S[(int64_t)f * d + c] += p[f] * vb[t * d + c];
+                }
+            }
+        }
+        /* keys: G, Gz hold the blocks after m, so walk the blocks backwards */
+        double *G = S, *Gz = Z;
+        memset(G, 0, sizeof(double) * (size_t)P2 * d);
+        memset(Gz, 0, sizeof(double) * (size_t)P2);
+        for (int m = n_blocks - 1; m >= 0; --m) {
+            const int64_t t0 = (int64_t)m * L;
+            for (int64_t t = t0; t < t0 + L; ++t) {
+                const double *kt = kb + t * d, *vt = vb + t * d;
+                phi_row(d, F, kt, Wh, u, p);
+                for (int f = 0; f < P2; ++f) {
+                    double acc = Gz[f];
+                    for (int c = 0; c < d; ++c) acc += G[(int64_t)f * d + c] * vt[c];
+                    dp[f] = acc;
+                }
+                phi_backward(F, p, dp, du);
+                for (int r = 0; r < d; ++r)
+                    for (int f = 0; f < F; ++f) gW[(int64_t)r * F + f] += kt[r] * du[f];
+            }
+            for (int64_t i = t0; i < t0 + L; ++i) {
+                const double *ph = phq + i * P2;
+                for (int f = 0; f < P2; ++f) {
+                    Gz[f] += ph[f] * dden[i];
+                    for (int c = 0; c < d; ++c) G[(int64_t)f * d + c] += ph[f] * dnum[i * d + c];
+                }
+            }
+        }
+        pw[bh] *= w * (1.0 - w);
+        free(S); free(Z); free(phq); free(dnum); free(dden);
+        free(u); free(p); free(dp); free(du); free(smn); free(o);
+    }
+    double total = 0.0;
+    memset(dW, 0, sizeof(double) * (size_t)H * d * F);
+    memset(dalpha, 0, sizeof(double) * (size_t)H);
+    for (int64_t bh = 0; bh < nbh; ++bh) {
+        int h = (int)(bh % H);
+        total += pl[bh];
+        dalpha[h] += pw[bh];
+        for (int64_t e = 0; e < (int64_t)d * F; ++e) dW[(int64_t)h * d * F + e] += pW[bh * d * F + e];
+    }
+    *loss = total;
+    free(pW); free(pw); free(pl);
+    return bad ? 3 : 0;
+}
