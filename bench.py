@@ -171,6 +171,37 @@ def comparator_sweep(args, torch, hba, wl, dev, B=128):
                       "rows": rows}), flush=True)
 
 
+def transfer_flops(d, F, L) -> int:
+    """Algorithmic flops of stage-1 attention transfer per (token, head):
+    phi(q) and phi(k) (2 x 2dF), block scores and A V (2 x 2Ld), the linear
+    readout and the commit (2 x 2(2F)d), dphi(q) and dphi(k) (2 x 2(2F)d),
+    the suffix state G (2(2F)d), and dW from the query and key sides (2 x 2dF)."""
+    return 2 * 2 * d * F + 2 * 2 * L * d + 5 * 2 * (2 * F) * d + 2 * 2 * d * F
+
+
+def transfer_bench(args, torch, hba, wl, dev):
+    """Stage-1 attention transfer: loss and dW, dalpha for 16 sequences of
+    2048 tokens (64 blocks of 32) x 16 heads, d = F = 128, bf16 inputs, fp32
+    arithmetic, against a synthetic teacher output."""
+    B, H, L, nb, d, F = 16, 16, 32, 64, 128, 128
+    N = nb * L
+    g = wl.generator(6_000_000, dev)
+    q, k, v = (wl.normal((B, H, N, d), 1.0, torch.bfloat16, g, dev) for _ in range(3))
+    W = wl.feature_weights(H, d, F, torch.bfloat16, g, dev)
+    alpha = torch.randn(H, generator=g, device=dev)
+    target = 0.3 * torch.randn((B, H, N, d), generator=g, device=dev)
+    ws = torch.empty(hba.transfer_workspace_bytes(B, H, L, d, F, nb) // 4, device=dev)
+    stream = torch.cuda.current_stream()
+    ms = _time_launches(torch, lambda: hba.transfer(q, k, v, W, alpha, target, L, workspace=ws), 2,
+                        max(3, min(args.steps, 10)), stream)
+    fl = transfer_flops(d, F, L) * B * H * N
+    print(json.dumps({"mode": "transfer", "batch": B, "heads": H, "tokens": N, "block": L, "head_dim": d,
+                      "feat": F, "dtype": "bf16 inputs, fp32 arithmetic (fp32 MFMA)", "ms": ms,
+                      "tokens_per_s": B * N / (ms * 1e-3), "algorithmic_flops": fl,
+                      "TFLOPs": fl / (ms * 1e-3) / 1e12, "fp32_mfma_peak_TFLOPs": 157.3,
+                      "frac_of_fp32_mfma_peak": fl / (ms * 1e-3) / 1e12 / 157.3}), flush=True)
+
+
 def decode_loop(args, torch, hba, wl, dev):
     """One hybrid layer through a block-diffusion decode: per 32-token block,
     8 denoising steps (hba_step) then hba_commit of the block; 32 requests."""
@@ -291,6 +322,8 @@ def main():
     ap.add_argument("--decode-loop", action="store_true",
                     help="time the B=32 decode loop (8 steps + 1 commit per 32-token block)")
     ap.add_argument("--blocks", type=int, default=256)
+    ap.add_argument("--transfer", action="store_true",
+                    help="time stage-1 attention transfer (loss, dW, dalpha) at 16 x 16 heads x 2048 tokens")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel (torch.neg) "
                          "10 times, to calibrate HBM byte counters")
@@ -322,6 +355,8 @@ def main():
         return
     if args.decode_loop:
         return decode_loop(args, torch, hba, wl, dev)
+    if args.transfer:
+        return transfer_bench(args, torch, hba, wl, dev)
     c = wl.serving_b128()
     B, H, L, d, F = c.batch, c.heads, c.block, c.head_dim, c.feat
     plen = torch.tensor(c.prefix, dtype=torch.int32)

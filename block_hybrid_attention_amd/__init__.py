@@ -23,7 +23,7 @@ from .pool import StatePool  # noqa: F401  (re-exported)
 
 __all__ = ["feature_map", "step", "commit", "prefix_softmax", "StatePool", "HbaError",
            "library_path", "load_library", "abi_version", "step_commit", "prefix_softmax_workspace_bytes",
-           "prefix_softmax_auto_split"]
+           "prefix_softmax_auto_split", "transfer", "transfer_workspace_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libhba.so")
@@ -75,11 +75,14 @@ def load_library():
         lib.hba_prefix_softmax_auto_split.restype = i32
         lib.hba_prefix_softmax_workspace_bytes.argtypes = [sp, i32]
         lib.hba_prefix_softmax_workspace_bytes.restype = i64
+        lib.hba_transfer.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
+        lib.hba_transfer_workspace_bytes.argtypes = [sp, i32]
+        lib.hba_transfer_workspace_bytes.restype = i64
         lib.hba_commit.argtypes = [sp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.hba_prefix_softmax.argtypes = [sp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.hba_step_commit.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         for fn in (lib.hba_feature_map, lib.hba_step, lib.hba_commit, lib.hba_prefix_softmax,
-                   lib.hba_step_commit, lib.hba_prefix_softmax_split):
+                   lib.hba_step_commit, lib.hba_prefix_softmax_split, lib.hba_transfer):
             fn.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -309,3 +312,52 @@ def prefix_softmax_auto_split(B, H, L, d, max_prefix, dtype=torch.bfloat16) -> i
     """The library's key-split choice for the current device."""
     shape = Shape(B, H, L, d, 64, _DTYPE[dtype], 0, 0)
     return int(load_library().hba_prefix_softmax_auto_split(ctypes.byref(shape), max_prefix))
+
+
+def transfer_workspace_bytes(B, H, block, d, F, n_blocks, dtype=torch.bfloat16) -> int:
+    """Workspace bytes of transfer() for this shape."""
+    shape = Shape(B, H, block, d, F, _DTYPE[dtype], 0, 0)
+    need = int(load_library().hba_transfer_workspace_bytes(ctypes.byref(shape), n_blocks))
+    if need < 0:
+        raise ValueError("unsupported shape for the transfer kernels (head_dim must be 128)")
+    return need
+
+
+def transfer(q, k, v, W, alpha, target, block, out=None, workspace=None, stream=None):
+    """Stage-1 attention transfer (section 3.2) of the hybrid layer (section
+    3.1) over whole sequences of N = n_blocks * block tokens: the summed
+    squared error against ``target`` and its gradients for W and alpha.
+
+    q, target [B][H][N][128] (target fp32); k, v [B][Hkv][N][128]; W [H][128][F];
+    alpha [H] fp32 (w = sigma(alpha)).  Returns (loss [1], dW [H][128][F],
+    dalpha [H], out) with out [B][H][N][128] fp32 when given (else None)."""
+    lib = load_library()
+    B, H, N, d = q.shape
+    F = W.shape[2]
+    dt = _in_dtype(q, k, v, W)
+    Hkv = _kv_heads(H, k)
+    if N % block:
+        raise ValueError(f"{N} tokens are not whole blocks of {block}")
+    nb = N // block
+    for t, nm in ((k, "k"), (v, "v")):
+        _check(t, (B, Hkv, N, d), q.dtype, nm)
+    _check(W, (H, d, F), q.dtype, "W")
+    _check(alpha, (H,), torch.float32, "alpha")
+    _check(target, (B, H, N, d), torch.float32, "target")
+    _check(out, (B, H, N, d), torch.float32, "out")
+    shape = Shape(B, H, block, d, F, dt, 0, Hkv)
+    need = int(lib.hba_transfer_workspace_bytes(ctypes.byref(shape), nb))
+    if need < 0:
+        raise ValueError("unsupported shape for the transfer kernels (head_dim must be 128)")
+    if workspace is None:
+        workspace = torch.empty((need + 3) // 4, device=q.device, dtype=torch.float32)
+    if workspace.dtype != torch.float32 or not workspace.is_contiguous() or workspace.numel() * 4 < need:
+        raise ValueError(f"workspace: need a contiguous fp32 tensor of at least {need} bytes")
+    loss = torch.empty(1, device=q.device, dtype=torch.float32)
+    dW = torch.empty((H, d, F), device=q.device, dtype=torch.float32)
+    dalpha = torch.empty(H, device=q.device, dtype=torch.float32)
+    _dev(q, k, v, W, alpha, target, out, workspace, loss)
+    _call(lib.hba_transfer, "hba_transfer", ctypes.byref(shape), nb, _p(q), _p(k), _p(v), _p(W), _p(alpha),
+          _p(target), _p(out), _p(loss), _p(dW), _p(dalpha), _p(workspace), workspace.numel() * 4,
+          _stream(stream))
+    return loss, dW, dalpha, out

@@ -72,7 +72,7 @@ const char *hba_status_string(hba_status st) {
     return "unknown status";
 }
 
-int32_t hba_abi_version(void) { return 4; }
+int32_t hba_abi_version(void) { return 5; }
 
 hba_status hba_feature_map(const hba_shape *shape, int64_t n_rows, const void *x, const void *W,
                            float *phi, void *stream) {
@@ -193,6 +193,36 @@ hba_status hba_prefix_softmax_split(const hba_shape *shape, int32_t max_prefix, 
                       n_split > 1 ? workspace : nullptr, n_split};
     return from_hip(hba::launch_prefix_softmax(a, shape->in_dtype == HBA_BF16, shape->head_dim,
                                                static_cast<hipStream_t>(stream)));
+}
+
+int64_t hba_transfer_workspace_bytes(const hba_shape *shape, int32_t n_blocks) {
+    if (check_common(shape, true, true) != HBA_OK || shape->head_dim != 128 || n_blocks < 0) return -1;
+    const int64_t N = (int64_t)n_blocks * shape->block;
+    return 4 * hba::transfer_workspace_floats((int64_t)shape->batch * shape->heads, N, shape->feat);
+}
+
+hba_status hba_transfer(const hba_shape *shape, int32_t n_blocks, const void *q, const void *k, const void *v,
+                        const void *W, const float *alpha, const float *target, float *out, float *loss,
+                        float *dW, float *dalpha, float *workspace, int64_t workspace_bytes, void *stream) {
+    hba_status st = check_common(shape, true, true);
+    if (st != HBA_OK) return st;
+    if (shape->head_dim != 128) return HBA_ERR_UNSUPPORTED;
+    const int G = kv_group(shape);
+    if (n_blocks < 0 || G == 0) return HBA_ERR_SHAPE;
+    const int64_t N = (int64_t)n_blocks * shape->block;
+    if (N > 0x7fffffff || (int64_t)shape->batch * shape->heads * N > ((int64_t)1 << 40)) return HBA_ERR_SHAPE;
+    if (!W || !alpha || !loss || !dW || !dalpha || !workspace) return HBA_ERR_NULL;
+    const bool work = shape->batch > 0 && n_blocks > 0;
+    if (work && (!q || !k || !v || !target)) return HBA_ERR_NULL;
+    if (workspace_bytes < hba_transfer_workspace_bytes(shape, n_blocks)) return HBA_ERR_CAPACITY;
+    if (!aligned16(W) || !aligned4(alpha) || !aligned4(loss) || !aligned16(dW) || !aligned4(dalpha) ||
+        !aligned16(workspace) || (out && !aligned16(out)) ||
+        (work && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(target))))
+        return HBA_ERR_ALIGN;
+    hba::TransferArgs a{q,   k,  v,      W,         alpha,        target,       out,         loss,
+                        dW,  dalpha, workspace, shape->batch, shape->heads, G, shape->block, n_blocks};
+    return from_hip(hba::launch_transfer(a, shape->in_dtype == HBA_BF16, shape->feat,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -72,6 +72,24 @@ struct PrefixArgs {
     int NS;
 };
 
+// Stage-1 attention transfer over sequences of nb blocks of L tokens
+// (N = nb L per (request, head)); head_dim 128.
+struct TransferArgs {
+    const void *q;           // [B][H][N][d]
+    const void *k, *v;       // [B][H/G][N][d]
+    const void *W;           // [H][d][F]
+    const float *alpha;      // [H]
+    const float *target;     // [B][H][N][d]
+    float *out;              // [B][H][N][d] or null
+    float *loss;             // [1]
+    float *dW;               // [H][d][F]
+    float *dalpha;           // [H]
+    float *ws;               // workspace, transfer_workspace_floats(B H, N, F) floats
+    int B, H, G, L, nb;
+};
+int64_t transfer_workspace_floats(int64_t BH, int64_t N, int F);
+hipError_t launch_transfer(const TransferArgs &a, bool dtype_bf16, int F, hipStream_t stream);
+
 // Largest key split of the comparator.
 constexpr int kMaxPrefixSplit = 64;
 

@@ -217,11 +217,50 @@ int32_t hba_prefix_softmax_auto_split(const hba_shape *shape, int32_t max_prefix
  * 4 B H n_split L (d + 2) otherwise, -1 for an invalid shape or n_split. */
 int64_t hba_prefix_softmax_workspace_bytes(const hba_shape *shape, int32_t n_split);
 
+/* Stage-1 attention transfer (section 3.2): for the hybrid layer of section
+ * 3.1 run over whole training sequences of N = n_blocks * block tokens per
+ * (request, head) -- the queries of block n see exact softmax over block n
+ * and the states S, Z of blocks 0..n-1 through the shared normaliser, gate
+ * w = sigma(alpha[h]) -- the summed squared error against the frozen
+ * softmax teacher's output and its gradient with respect to the layer's own
+ * parameters:
+ *   loss      = sum over b, h, tokens, columns of (out - target)^2
+ *   dW[h]     = d loss / d W[h],   dalpha[h] = d loss / d alpha[h]
+ * q, k, v and target are inputs (the backbone is frozen); the gradient flows
+ * through the shared normaliser, phi(q), the states and phi(k).
+ * Arithmetic is fp32 throughout (fp32 matrix cores).  head_dim 128 only.
+ * Reads: batch, heads, block, head_dim, feat, in_dtype, kv_heads.
+ *   q, target  [B][H][N][128]      q in_dtype, target fp32
+ *   k, v       [B][Hkv][N][128]    in_dtype
+ *   W          [H][128][F]         in_dtype
+ *   alpha      [H] fp32            the gate parameter, w = sigma(alpha)
+ *   out        [B][H][N][128] fp32 the layer's output, or NULL
+ *   loss       [1] fp32            overwritten
+ *   dW         [H][128][F] fp32    overwritten
+ *   dalpha     [H] fp32            overwritten
+ *   workspace  caller-owned device scratch of at least
+ *              hba_transfer_workspace_bytes(shape, n_blocks) bytes,
+ *              16-byte aligned; contents on entry do not matter.  Calls in
+ *              flight at the same time need separate workspaces.
+ * The per-(request, head) parts are summed over requests in request order:
+ * the same inputs give bitwise-equal results.  batch = 0 or n_blocks = 0
+ * writes zeros.
+ * Errors: HBA_ERR_UNSUPPORTED for head_dim != 128; HBA_ERR_CAPACITY for a
+ * workspace that is too small; otherwise as hba_step. */
+hba_status hba_transfer(const hba_shape *shape, int32_t n_blocks, const void *q, const void *k,
+                        const void *v, const void *W, const float *alpha, const float *target, float *out,
+                        float *loss, float *dW, float *dalpha, float *workspace, int64_t workspace_bytes,
+                        void *stream);
+
+/* Workspace bytes of hba_transfer (4 B (N (d + 1) + 2 d F + 4) rounded),
+ * -1 for an unsupported shape. */
+int64_t hba_transfer_workspace_bytes(const hba_shape *shape, int32_t n_blocks);
+
 /* Static description of a status code (never NULL). */
 const char *hba_status_string(hba_status status);
 
-/* Library ABI version, currently 4 (2 added hba_step_commit, 3 added
- * hba_shape.kv_heads, 4 added the split comparator). */
+/* Library ABI version, currently 5 (2 added hba_step_commit, 3 added
+ * hba_shape.kv_heads, 4 added the split comparator, 5 hba_transfer). */
 int32_t hba_abi_version(void);
 
 #ifdef __cplusplus

@@ -38,11 +38,12 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"hba_feature_map", "hba_step", "hba_commit", "hba_prefix_softmax", "hba_step_commit",
             "hba_prefix_softmax_split", "hba_prefix_softmax_auto_split", "hba_prefix_softmax_workspace_bytes",
+            "hba_transfer", "hba_transfer_workspace_bytes",
             "hba_status_string", "hba_abi_version"} <= set(names)
     L = lib()
     for n in names:
         assert hasattr(L, n), n
-    assert hba.abi_version() == 4
+    assert hba.abi_version() == 5
 
 
 def test_status_strings():
@@ -199,6 +200,30 @@ def test_split_comparator_validation():
     # without a device the choice falls back to one split; bad shapes give 1 too
     assert L.hba_prefix_softmax_auto_split(ctypes.byref(sh), 1 << 15) == 1
     assert L.hba_prefix_softmax_auto_split(None, 128) == 1
+
+
+@no_gpu_only
+def test_transfer_validation():
+    L = lib()
+
+    def call(sh, nb=4, q=A, W=A, alpha=A, loss=A2, ws=A2, wsb=1 << 40, target=A):
+        return L.hba_transfer(ctypes.byref(sh), nb, q, A, A, W, alpha, target, None, loss, A2, A2, ws, wsb, None)
+
+    sh = shape()
+    need = L.hba_transfer_workspace_bytes(ctypes.byref(sh), 4)
+    N = 4 * 32
+    assert need == 4 * (2 * 4 * N * 128 + 2 * 4 * N + 2 * 2 * 4 * 128 * 128 + 4 * 2 * 4)
+    assert L.hba_transfer_workspace_bytes(ctypes.byref(shape(d=64)), 4) == -1
+    assert call(shape(d=64)) == EUNSUP
+    assert call(shape(F=96)) == EUNSUP
+    assert call(sh, nb=-1) == ESHAPE
+    assert call(shape(kv_heads=3)) == ESHAPE
+    assert call(sh, q=None) == ENULL
+    assert call(sh, ws=None) == ENULL
+    assert call(sh, loss=None) == ENULL
+    assert call(sh, wsb=need - 4) == ECAP
+    assert call(sh, W=MIS) == EALIGN
+    assert call(sh, target=MIS) == EALIGN
 
 
 def test_python_binding_refuses_host_tensors():
