@@ -69,16 +69,19 @@ struct XferGeom {
 };
 
 // Workspace layout (floats), per (request, head) pair bh of BH:
-//   dnum [BH][N][d], dden [BH][Npad], dWq [BH][d][F], dWk [BH][d][F], scal [BH][4]
+//   dnum [BH][N][d], dden [BH][Npad], phq, phk [BH][N][2F] (phi(q), phi(k)
+//   from the forward sweep), dWq [BH][d][F], dWk [BH][d][F], scal [BH][4]
 struct XferWs {
-    int64_t dnum, dden, dWq, dWk, scal, total;
+    int64_t dnum, dden, phq, phk, dWq, dWk, scal, total;
 };
 __host__ __device__ inline XferWs xfer_ws(int64_t BH, int64_t N, int F) {
     const int64_t npad = (N + 3) & ~int64_t(3);
     XferWs w;
     w.dnum = 0;
     w.dden = w.dnum + BH * N * kXferD;
-    w.dWq = w.dden + BH * npad;
+    w.phq = w.dden + BH * npad;
+    w.phk = w.phq + BH * N * 2 * F;
+    w.dWq = w.phk + BH * N * 2 * F;
     w.dWk = w.dWq + BH * kXferD * F;
     w.scal = w.dWk + BH * kXferD * F;
     w.total = w.scal + BH * 4;
@@ -127,6 +130,26 @@ __device__ __forceinline__ void stage_cols_f32(const T *__restrict__ rows, int n
     const int row = tid >> 4, c0 = (tid & 15) * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dstT[(c0 + e) * TLD + row] = x[e];
+}
+
+// 32 fp32 rows of COLS columns (row stride COLS) into the transposed tile
+// dstT[COLS][TLD]; rows >= nrows become zero.
+template <int COLS, int TLD>
+__device__ __forceinline__ void stage_colsT_f32(const float *__restrict__ rows, int nrows, float *dstT, int tid) {
+    constexpr int TPR = COLS / 8;                  // threads per row, eight columns each
+    constexpr int RPP = kXferThreads / TPR;        // rows per pass
+#pragma unroll
+    for (int p = 0; p < kRows / RPP; ++p) {
+        const int row = p * RPP + tid / TPR, c0 = (tid % TPR) * 8;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+        if (row < nrows) {
+            a = *reinterpret_cast<const float4 *>(rows + (int64_t)row * COLS + c0);
+            b = *reinterpret_cast<const float4 *>(rows + (int64_t)row * COLS + c0 + 4);
+        }
+        const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dstT[(c0 + e) * TLD + row] = x[e];
+    }
 }
 
 // W columns 16 ct .. 16 ct + 15 as the B operand of u = x W: wr[ks] = W[4 ks + lg][16 ct + li].
@@ -272,7 +295,6 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_kernel(Trans
         stage_cols_f32<T, TLD>(vg + t0 * D, L, vT, tid);
         __syncthreads();
         phi_qk<F>(xq, xk, wr, phqT, phkT, red, L, wave, li, lg);
-
         if (wave < 4) {
             // scores of query tile it against key tile jt, in log2 units; keys >= L masked
             const int it = wave >> 1, jt = wave & 1;
@@ -402,6 +424,26 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_kernel(Trans
                 S[ft] = mfma_f32(phkT[(16 * ft + li) * TLD + 4 * ks + lg], vT[(c0 + li) * TLD + 4 * ks + lg], S[ft]);
             fence();
         }
+        {
+            // phi(q), phi(k) rows of this block to the workspace: the gradient
+            // sweeps read them instead of recomputing both maps
+            constexpr int PER = P2 / 16;   // columns per thread: 16 threads per row
+            const int row = tid >> 4, f0 = (tid & 15) * PER;
+            if (row < L) {
+                float *gq = a.ws + ws.phq + (bh * N + t0 + row) * P2 + f0;
+                float *gk = a.ws + ws.phk + (bh * N + t0 + row) * P2 + f0;
+#pragma unroll
+                for (int e = 0; e < PER; e += 4) {
+                    *reinterpret_cast<float4 *>(gq + e) =
+                        make_float4(phqT[(f0 + e) * TLD + row], phqT[(f0 + e + 1) * TLD + row],
+                                    phqT[(f0 + e + 2) * TLD + row], phqT[(f0 + e + 3) * TLD + row]);
+                    *reinterpret_cast<float4 *>(gk + e) =
+                        make_float4(phkT[(f0 + e) * TLD + row], phkT[(f0 + e + 1) * TLD + row],
+                                    phkT[(f0 + e + 2) * TLD + row], phkT[(f0 + e + 3) * TLD + row]);
+                    fence();
+                }
+            }
+        }
         __syncthreads();
     }
     // per-(request, head) loss and dL/dw (dw lives in the lanes of threads 256 .. 287)
@@ -453,9 +495,9 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_sweep_kernel(Transfe
     const XferWs ws = xfer_ws((int64_t)a.B * a.H, N, F);
     const float *dng = a.ws + ws.dnum + bh * N * D;
     const float *ddg = a.ws + ws.dden + bh * npad;
-
-    float wr[D / 4];
-    load_w_cols<T, F>(static_cast<const T *>(a.W) + (int64_t)h * D * F, F == 128 ? wave : (wave & 3), li, lg, wr);
+    const float *pqg = a.ws + ws.phq + bh * N * P2;
+    const float *pkg = a.ws + ws.phk + bh * N * P2;
+    (void)h;
     const int fb = wave * FS;
     floatx4 X[D / 16][FT];   // X^T[16 ct + 4 lg + r][fb + 16 j + li]
 #pragma unroll
@@ -473,13 +515,17 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_sweep_kernel(Transfe
     for (int it_ = 0; it_ < a.nb; ++it_) {
         const int n = KEYS ? a.nb - 1 - it_ : it_;
         const int64_t t0 = (int64_t)n * L;
-        stage_rows_f32<T, G::XLD>(qg + t0 * D, L, xq, tid);
-        stage_rows_f32<T, G::XLD>(kg + t0 * D, L, xk, tid);
+        // only the side whose gradient this sweep takes needs its rows
+        if (KEYS)
+            stage_rows_f32<T, G::XLD>(kg + t0 * D, L, xk, tid);
+        else
+            stage_rows_f32<T, G::XLD>(qg + t0 * D, L, xq, tid);
         stage_cols_f32<T, TLD>(vg + t0 * D, L, vT, tid);
         stage_cols_f32<float, TLD>(dng + t0 * D, L, dnT, tid);
+        stage_colsT_f32<P2, TLD>(pqg + t0 * P2, L, phqT, tid);
+        stage_colsT_f32<P2, TLD>(pkg + t0 * P2, L, phkT, tid);
         if (tid < kRows) dd[tid] = tid < L ? ddg[t0 + tid] : 0.f;
         __syncthreads();
-        phi_qk<F>(xq, xk, wr, phqT, phkT, red, L, wave, li, lg);
 
         float *phx = KEYS ? phkT : phqT;        // the side whose gradient this sweep takes
         const float *phy = KEYS ? phqT : phkT;  // the side folded into the state

@@ -252,7 +252,8 @@ hba_status hba_transfer(const hba_shape *shape, int32_t n_blocks, const void *q,
                         float *loss, float *dW, float *dalpha, float *workspace, int64_t workspace_bytes,
                         void *stream);
 
-/* Workspace bytes of hba_transfer (4 B (N (d + 1) + 2 d F + 4) rounded),
+/* Workspace bytes of hba_transfer (4 B H (N (d + 1 + 4F) + 2 d F + 4), N
+ * rounded up to a multiple of 4 in the second term),
  * -1 for an unsupported shape. */
 int64_t hba_transfer_workspace_bytes(const hba_shape *shape, int32_t n_blocks);
 

@@ -212,7 +212,8 @@ def test_transfer_validation():
     sh = shape()
     need = L.hba_transfer_workspace_bytes(ctypes.byref(sh), 4)
     N = 4 * 32
-    assert need == 4 * (2 * 4 * N * 128 + 2 * 4 * N + 2 * 2 * 4 * 128 * 128 + 4 * 2 * 4)
+    # dnum, dden, phi(q) and phi(k), two dW parts, four scalars per (request, head)
+    assert need == 4 * (2 * 4 * N * 128 + 2 * 4 * N + 2 * 2 * 4 * N * 256 + 2 * 2 * 4 * 128 * 128 + 4 * 2 * 4)
     assert L.hba_transfer_workspace_bytes(ctypes.byref(shape(d=64)), 4) == -1
     assert call(shape(d=64)) == EUNSUP
     assert call(shape(F=96)) == EUNSUP

@@ -347,8 +347,13 @@ def test_int64_state_offsets():
     Sr, Zr = oracle.commit(*host_pool(1, H, F, d), k1, v1, W)
     ref = oracle.step(q, k, v, W, Sr, Zr)
     errs = dict(S=state_rel(S[n_slots - 1:], Sr), out=row_rel(out, ref))
+    # the fused last step + commit on the same far slot
+    out2 = hba.step_commit(q, k, v, W, S, Z, slot=slot)
+    Sr2, Zr2 = oracle.commit(Sr, Zr, k, v, W)
+    errs.update(fused_out=row_rel(out2, ref), fused_S=state_rel(S[n_slots - 1:], Sr2),
+                fused_Z=state_rel(Z[n_slots - 1:, :, :, None], Zr2[..., None]))
     report("int64 offsets", **errs)
-    assert float(S[: n_slots - 1].abs().max()) == 0.0
+    assert float(S[: n_slots - 1].abs().max()) == 0.0 and float(Z[: n_slots - 1].abs().max()) == 0.0
     for e in errs.values():
         assert e <= TOL[dt]
     del S, Z
