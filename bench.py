@@ -196,7 +196,7 @@ def transfer_bench(args, torch, hba, wl, dev):
                         max(3, min(args.steps, 10)), stream)
     fl = transfer_flops(d, F, L) * B * H * N
     print(json.dumps({"mode": "transfer", "batch": B, "heads": H, "tokens": N, "block": L, "head_dim": d,
-                      "feat": F, "dtype": "bf16 inputs, fp32 arithmetic (fp32 MFMA)", "ms": ms,
+                      "feat": F, "dtype": "bf16 inputs, fp32 arithmetic (fp32 MFMA; the feature map on bf16 MFMA, exact products)", "ms": ms,
                       "tokens_per_s": B * N / (ms * 1e-3), "algorithmic_flops": fl,
                       "TFLOPs": fl / (ms * 1e-3) / 1e12, "fp32_mfma_peak_TFLOPs": 157.3,
                       "frac_of_fp32_mfma_peak": fl / (ms * 1e-3) / 1e12 / 157.3}), flush=True)

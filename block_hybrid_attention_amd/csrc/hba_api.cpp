@@ -83,7 +83,8 @@ hba_status hba_feature_map(const hba_shape *shape, int64_t n_rows, const void *x
     if (n_rows == 0) return HBA_OK;
     if (!x || !W || !phi) return HBA_ERR_NULL;
     if (!aligned16(x) || !aligned16(W) || !aligned16(phi)) return HBA_ERR_ALIGN;
-    hba::FeatureMapArgs a{x, W, phi, n_rows, shape->heads};
+    const int64_t H = shape->heads, d = shape->head_dim, P2 = 2 * shape->feat;
+    hba::FeatureMapArgs a{x, W, phi, n_rows, shape->heads, H * d, d, 0, H * P2, P2, 0, 1};
     return from_hip(hba::launch_feature_map(a, shape->in_dtype == HBA_BF16, shape->head_dim,
                                             shape->feat, static_cast<hipStream_t>(stream)));
 }
@@ -211,6 +212,7 @@ hba_status hba_transfer(const hba_shape *shape, int32_t n_blocks, const void *q,
     if (n_blocks < 0 || G == 0) return HBA_ERR_SHAPE;
     const int64_t N = (int64_t)n_blocks * shape->block;
     if (N > 0x7fffffff || (int64_t)shape->batch * shape->heads * N > ((int64_t)1 << 40)) return HBA_ERR_SHAPE;
+    if (shape->batch > 65535) return HBA_ERR_SHAPE;   // the feature-map pass runs one grid layer per request
     if (!W || !alpha || !loss || !dW || !dalpha || !workspace) return HBA_ERR_NULL;
     const bool work = shape->batch > 0 && n_blocks > 0;
     if (work && (!q || !k || !v || !target)) return HBA_ERR_NULL;

@@ -27,11 +27,12 @@ __global__ __launch_bounds__(kThreads) void feature_map_kernel(FeatureMapArgs a)
     const int64_t left = a.n - r0;
     const int nrows = left < kRows ? (int)left : kRows;
 
-    const T *xg = static_cast<const T *>(a.x) + (r0 * a.H + h) * D;
+    const int64_t bz = blockIdx.z;
+    const T *xg = static_cast<const T *>(a.x) + bz * a.xs_b + (int64_t)(h / a.G) * a.xs_h + r0 * a.xs_r;
     const T *Wg = static_cast<const T *>(a.W) + (int64_t)h * D * F;
     WChunks<T, D, F> wc;
     load_w<T, D, F>(Wg, wc);
-    stage_rows<T, D, F>(xg, (int64_t)a.H * D, nrows, xs);
+    stage_rows<T, D, F>(xg, a.xs_r, nrows, xs);
     store_w<T, D, F>(wc, ws);
     __syncthreads();
     project_tile<T, D, F>(xs, ws, us);
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void feature_map_kernel(FeatureMapArgs a)
         if (i >= nrows) break;
         float pp[FM], pn[FM];
         phi_of_row<F>(us + i * P::ULD, lane, pp, pn);
-        float *o = a.phi + ((r0 + i) * a.H + h) * (2 * F);
+        float *o = a.phi + bz * a.ps_b + (int64_t)h * a.ps_h + (r0 + i) * a.ps_r;
 #pragma unroll
         for (int m = 0; m < FM; ++m) {
             o[lane + 64 * m] = pp[m];
@@ -87,12 +88,13 @@ __global__ __launch_bounds__(kThreads, 2) void feature_map_kernel_bf16(FeatureMa
     const int h = (int)blockIdx.y;
     const int64_t n = a.n;
     const int64_t tile0 = (int64_t)blockIdx.x * kFmTiles;
-    const T *xg = static_cast<const T *>(a.x);
+    const int64_t bz = blockIdx.z;
+    const T *xg = static_cast<const T *>(a.x) + bz * a.xs_b + (int64_t)(h / a.G) * a.xs_h;
 
     auto load_x = [&](int64_t r0, bf16x8 (&xo)[KS]) {
         int64_t row = r0 + 16 * qgrp + li;
         row = row < n ? row : n - 1;   // rows past the end repeat the last one (not stored)
-        const T *p = xg + (row * a.H + h) * D + 8 * lg;
+        const T *p = xg + row * a.xs_r + 8 * lg;
 #pragma unroll
         for (int s_ = 0; s_ < KS; ++s_) xo[s_] = *reinterpret_cast<const bf16x8 *>(p + 32 * s_);
     };
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(kThreads, 2) void feature_map_kernel_bf16(FeatureMa
         for (int ii = 0; ii < kRows / 4; ++ii) {
             const int i = 4 * ii + wave;
             if (i < nrows) {
-                float *o = a.phi + ((r0 + i) * a.H + h) * (2 * F);
+                float *o = a.phi + bz * a.ps_b + (int64_t)h * a.ps_h + (r0 + i) * a.ps_r;
 #pragma unroll
                 for (int e = lane; e < RV; e += kWave)
                     __builtin_nontemporal_store(*reinterpret_cast<const floatx4 *>(ph + i * G::PLD + 4 * e),
@@ -171,20 +173,21 @@ __global__ __launch_bounds__(kThreads, 2) void feature_map_kernel_bf16(FeatureMa
 }
 
 template <typename T, int D, int F>
-static hipError_t launch_fm_t(const FeatureMapArgs &a, hipStream_t stream) {
+static hipError_t launch_fm_t(const FeatureMapArgs &a, unsigned batches, hipStream_t stream) {
     const int64_t tiles = (a.n + kRows - 1) / kRows;
     if constexpr (sizeof(T) == 2) {
         const unsigned groups = (unsigned)((tiles + kFmTiles - 1) / kFmTiles);
-        return launch_kernel(feature_map_kernel_bf16<D, F>, dim3(groups, (unsigned)a.H), dim3(kThreads), a, stream);
+        return launch_kernel(feature_map_kernel_bf16<D, F>, dim3(groups, (unsigned)a.H, batches), dim3(kThreads), a, stream);
     } else {
-        return launch_kernel(feature_map_kernel<T, D, F>, dim3((unsigned)tiles, (unsigned)a.H), dim3(kThreads), a, stream);
+        return launch_kernel(feature_map_kernel<T, D, F>, dim3((unsigned)tiles, (unsigned)a.H, batches), dim3(kThreads), a, stream);
     }
 }
 
-hipError_t launch_feature_map(const FeatureMapArgs &a, bool bf16, int d, int F, hipStream_t stream) {
+hipError_t launch_feature_map(const FeatureMapArgs &a, bool bf16, int d, int F, hipStream_t stream, int batches) {
+    const unsigned nb = (unsigned)batches;
 #define HBA_FM_CASE(DD, FF)                                                                \
     if (d == DD && F == FF)                                                                \
-        return bf16 ? launch_fm_t<uint16_t, DD, FF>(a, stream) : launch_fm_t<float, DD, FF>(a, stream);
+        return bf16 ? launch_fm_t<uint16_t, DD, FF>(a, nb, stream) : launch_fm_t<float, DD, FF>(a, nb, stream);
     HBA_FM_CASE(64, 64)
     HBA_FM_CASE(64, 128)
     HBA_FM_CASE(128, 64)

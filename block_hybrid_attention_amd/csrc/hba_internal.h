@@ -8,12 +8,19 @@
 
 namespace hba {
 
+// Row r of head h in batch b (b < gridDim.z) reads x at
+// b xs_b + (h / G) xs_h + r xs_r and writes phi at b ps_b + h ps_h + r ps_r.
+// The public call uses x [n][H][d], phi [n][H][2F] (xs_r = H d, xs_h = d,
+// ps_r = 2F H, ps_h = 2F, one batch, G = 1).
 struct FeatureMapArgs {
-    const void *x;       // [n][H][d]
+    const void *x;
     const void *W;       // [H][d][F]
-    float *phi;          // [n][H][2F]
+    float *phi;
     int64_t n;
     int H;
+    int64_t xs_r, xs_h, xs_b;   // x strides (elements)
+    int64_t ps_r, ps_h, ps_b;   // phi strides (floats)
+    int G;                      // query heads per key/value head of x
 };
 
 // Key/value inputs are [B][H/G][...][d]: query head h of request b reads
@@ -107,8 +114,8 @@ inline hipError_t launch_kernel(void (*k)(Args), dim3 grid, dim3 block, const Ar
 
 // Each launcher enqueues one kernel on `stream`; dtype_bf16 selects the
 // element type of the inputs.  Returns the launch status.
-hipError_t launch_feature_map(const FeatureMapArgs &a, bool dtype_bf16, int d, int F,
-                              hipStream_t stream);
+hipError_t launch_feature_map(const FeatureMapArgs &a, bool dtype_bf16, int d, int F, hipStream_t stream,
+                              int batches = 1);
 hipError_t launch_step(const StepArgs &a, bool dtype_bf16, int d, int F, hipStream_t stream);
 hipError_t launch_commit(const CommitArgs &a, bool dtype_bf16, int d, int F, hipStream_t stream);
 hipError_t launch_step_commit(const StepCommitArgs &a, bool dtype_bf16, int d, int F, hipStream_t stream);

@@ -18,8 +18,13 @@
 //   du = p (dp - p.dp) - p' (dp' - p'.dp')  for phi = [p, p'] = [softmax(u), softmax(-u)],
 //   dW += x du^T for every query row and key row x.
 //
-// Four launches, one workgroup of eight waves per (request, head) for the
-// three sweeps over the blocks:
+// Six launches:
+//   0. the feature map (hba_feature_map's kernels) of every query and key
+//      row into the workspace, fully parallel over rows; bf16 inputs run on
+//      bf16 MFMA, whose products of bf16 values are exact.  The three sweeps
+//      below stage phi from there instead of computing it per block.
+// then one workgroup of eight waves per (request, head) for the three sweeps
+// over the blocks:
 //   1. forward sweep: output, loss, dnum and dden (stored to the workspace)
 //      and dL/dw.  S (2F x d) lives in registers split by value column,
 //      the layout in which phi(q) S contracts over features.
@@ -30,8 +35,8 @@
 //      after each block with phi(q)^T dnum; into dW.
 //   4. reduction of the per-(request, head) parts over requests, in request
 //      order (deterministic).
-// Every product runs on fp32 MFMA (v_mfma_f32_16x16x4f32), so the
-// arithmetic is fp32 throughout; bf16 inputs are widened when staged.
+// Every product of the sweeps runs on fp32 MFMA (v_mfma_f32_16x16x4f32), so
+// the arithmetic is fp32 throughout; bf16 inputs are widened when staged.
 // Token tiles that MFMA reads with the token index on the 16-lane axis are
 // staged transposed in LDS ([column][32 tokens + 4]); that stride puts the
 // 64 lanes of an operand read on 64 different banks.
@@ -152,107 +157,6 @@ __device__ __forceinline__ void stage_colsT_f32(const float *__restrict__ rows, 
     }
 }
 
-// W columns 16 ct .. 16 ct + 15 as the B operand of u = x W: wr[ks] = W[4 ks + lg][16 ct + li].
-template <typename T, int F>
-__device__ __forceinline__ void load_w_cols(const T *__restrict__ Wh, int ct, int li, int lg, float (&wr)[kXferD / 4]) {
-#pragma unroll
-    for (int ks = 0; ks < kXferD / 4; ++ks) wr[ks] = to_f32(Wh[(int64_t)(4 * ks + lg) * F + 16 * ct + li]);
-}
-
-// phi of the 32 staged rows of q and of k (section 3.1), written transposed
-// to phqT / phkT [2F][TLD]; rows >= L are written as zero.  Each wave
-// projects one 16-column tile of u = x W for both q and k (F = 128) or for
-// one of them (F = 64: waves 0-3 q, 4-7 k); the row max, min and sums cross
-// the column tiles through LDS.
-template <int F>
-__device__ __forceinline__ void phi_qk(const float *xq, const float *xk, const float (&wr)[kXferD / 4],
-                                       float *phqT, float *phkT, float *red, int L, int wave, int li,
-                                       int lg) {
-    using G = XferGeom<F>;
-    constexpr int NX = F == 128 ? 2 : 1;       // tiles of x (q, k) per wave
-    constexpr int NCT = F / 16;                // column tiles of u per row
-    const int ct = F == 128 ? wave : (wave & 3);
-    floatx4 u[NX][2];
-#pragma unroll
-    for (int xi = 0; xi < NX; ++xi) {
-        const int x = NX == 2 ? xi : (wave >> 2);
-        const float *xs = x == 0 ? xq : xk;
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < kXferD / 4; ++ks) {
-                acc = mfma_f32(xs[(16 * rt + li) * G::XLD + 4 * ks + lg], wr[ks], acc);
-                if ((ks & 7) == 7) fence();
-            }
-            u[xi][rt] = acc;
-        }
-    }
-    auto R = [&](int kind, int x, int c, int row) -> float & { return red[((kind * 2 + x) * 8 + c) * kRows + row]; };
-#pragma unroll
-    for (int xi = 0; xi < NX; ++xi) {
-        const int x = NX == 2 ? xi : (wave >> 2);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float mx = row16_max(u[xi][rt][r]), mn = row16_min(u[xi][rt][r]);
-                if (li == 0) {
-                    R(0, x, ct, 16 * rt + 4 * lg + r) = mx;
-                    R(1, x, ct, 16 * rt + 4 * lg + r) = mn;
-                }
-            }
-    }
-    __syncthreads();
-    floatx4 en[NX][2];
-#pragma unroll
-    for (int xi = 0; xi < NX; ++xi) {
-        const int x = NX == 2 ? xi : (wave >> 2);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * rt + 4 * lg + r;
-                float M = R(0, x, 0, row), Mn = R(1, x, 0, row);
-#pragma unroll
-                for (int c = 1; c < NCT; ++c) {
-                    M = fmaxf(M, R(0, x, c, row));
-                    Mn = fminf(Mn, R(1, x, c, row));
-                }
-                const float uu = u[xi][rt][r];
-                u[xi][rt][r] = fast_exp(uu - M);
-                en[xi][rt][r] = fast_exp(Mn - uu);
-                const float sp = row16_sum(u[xi][rt][r]), sn = row16_sum(en[xi][rt][r]);
-                if (li == 0) {
-                    R(2, x, ct, row) = sp;
-                    R(3, x, ct, row) = sn;
-                }
-            }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int xi = 0; xi < NX; ++xi) {
-        const int x = NX == 2 ? xi : (wave >> 2);
-        float *phT = x == 0 ? phqT : phkT;
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * rt + 4 * lg + r;
-                float sp = 0.f, sn = 0.f;
-#pragma unroll
-                for (int c = 0; c < NCT; ++c) {
-                    sp += R(2, x, c, row);
-                    sn += R(3, x, c, row);
-                }
-                const bool ok = row < L;
-                phT[(16 * ct + li) * G::TLD + row] = ok ? u[xi][rt][r] / sp : 0.f;
-                phT[(F + 16 * ct + li) * G::TLD + row] = ok ? en[xi][rt][r] / sn : 0.f;
-            }
-    }
-    __syncthreads();
-}
-
 // 1. Forward sweep.
 template <typename T, int F>
 __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_kernel(TransferArgs a) {
@@ -278,8 +182,8 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_kernel(Trans
     constexpr float kScaleLog2 = 0.08838834764831845f * 1.4426950408889634f;   // log2(e) / sqrt(128)
     const XferWs ws = xfer_ws((int64_t)a.B * a.H, N, F);
 
-    float wr[D / 4];
-    load_w_cols<T, F>(static_cast<const T *>(a.W) + (int64_t)h * D * F, F == 128 ? wave : (wave & 3), li, lg, wr);
+    const float *pqg = a.ws + ws.phq + bh * N * P2;
+    const float *pkg = a.ws + ws.phk + bh * N * P2;
     floatx4 S[NFT];   // S[16 ft + 4 lg + r][16 wave + li]
 #pragma unroll
     for (int ft = 0; ft < NFT; ++ft) S[ft] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -293,8 +197,9 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_kernel(Trans
         stage_rows_f32<T, G::XLD>(qg + t0 * D, L, xq, tid);
         stage_rows_f32<T, G::XLD>(kg + t0 * D, L, xk, tid);
         stage_cols_f32<T, TLD>(vg + t0 * D, L, vT, tid);
+        stage_colsT_f32<P2, TLD>(pqg + t0 * P2, L, phqT, tid);
+        stage_colsT_f32<P2, TLD>(pkg + t0 * P2, L, phkT, tid);
         __syncthreads();
-        phi_qk<F>(xq, xk, wr, phqT, phkT, red, L, wave, li, lg);
         if (wave < 4) {
             // scores of query tile it against key tile jt, in log2 units; keys >= L masked
             const int it = wave >> 1, jt = wave & 1;
@@ -423,26 +328,6 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_kernel(Trans
             for (int ks = 0; ks < kRows / 4; ++ks)
                 S[ft] = mfma_f32(phkT[(16 * ft + li) * TLD + 4 * ks + lg], vT[(c0 + li) * TLD + 4 * ks + lg], S[ft]);
             fence();
-        }
-        {
-            // phi(q), phi(k) rows of this block to the workspace: the gradient
-            // sweeps read them instead of recomputing both maps
-            constexpr int PER = P2 / 16;   // columns per thread: 16 threads per row
-            const int row = tid >> 4, f0 = (tid & 15) * PER;
-            if (row < L) {
-                float *gq = a.ws + ws.phq + (bh * N + t0 + row) * P2 + f0;
-                float *gk = a.ws + ws.phk + (bh * N + t0 + row) * P2 + f0;
-#pragma unroll
-                for (int e = 0; e < PER; e += 4) {
-                    *reinterpret_cast<float4 *>(gq + e) =
-                        make_float4(phqT[(f0 + e) * TLD + row], phqT[(f0 + e + 1) * TLD + row],
-                                    phqT[(f0 + e + 2) * TLD + row], phqT[(f0 + e + 3) * TLD + row]);
-                    *reinterpret_cast<float4 *>(gk + e) =
-                        make_float4(phkT[(f0 + e) * TLD + row], phkT[(f0 + e + 1) * TLD + row],
-                                    phkT[(f0 + e + 2) * TLD + row], phkT[(f0 + e + 3) * TLD + row]);
-                    fence();
-                }
-            }
         }
         __syncthreads();
     }
@@ -679,8 +564,19 @@ static hipError_t launch_transfer_t(const TransferArgs &a, hipStream_t stream) {
     const int64_t pairs = (int64_t)a.B * a.H;
     hipError_t e = hipSuccess;
     if (pairs > 0 && a.nb > 0) {
+        // phi(q) and phi(k) of every token first, fully parallel, into the
+        // workspace rows [B H][N][2F]; the three sweeps stage them from there
+        const int64_t N = (int64_t)a.nb * a.L, D = kXferD, P2 = 2 * F;
+        const XferWs ws = xfer_ws(pairs, N, F);
+        const FeatureMapArgs fq{a.q, a.W, a.ws + ws.phq, N, a.H, D, N * D, (int64_t)a.H * N * D,
+                                P2, N * P2, (int64_t)a.H * N * P2, 1};
+        const FeatureMapArgs fk{a.k, a.W, a.ws + ws.phk, N, a.H, D, N * D, (int64_t)(a.H / a.G) * N * D,
+                                P2, N * P2, (int64_t)a.H * N * P2, a.G};
+        constexpr bool bf16 = sizeof(T) == 2;
+        e = launch_feature_map(fq, bf16, (int)D, F, stream, a.B);
+        if (e == hipSuccess) e = launch_feature_map(fk, bf16, (int)D, F, stream, a.B);
         const dim3 grid((unsigned)pairs), block(kXferThreads);
-        e = launch_kernel(transfer_forward_kernel<T, F>, grid, block, a, stream);
+        if (e == hipSuccess) e = launch_kernel(transfer_forward_kernel<T, F>, grid, block, a, stream);
         if (e == hipSuccess) e = launch_kernel(transfer_sweep_kernel<T, F, false>, grid, block, a, stream);
         if (e == hipSuccess) e = launch_kernel(transfer_sweep_kernel<T, F, true>, grid, block, a, stream);
     }
