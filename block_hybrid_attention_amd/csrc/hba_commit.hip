@@ -194,8 +194,11 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(CommitArgs a) {
 //     one-block commits that buffer reuses the LDS of W.
 //   * Every wave owns F/4 state rows and adds phi(K)^T V on bf16 MFMA with phi
 //     split into a bf16 high part and residual (v is exact in bf16): two
-//     products per tile.  Each lane owns d/16 consecutive columns, so the
-//     state is read and written in whole 512-byte rows.
+//     products per tile.  N-tile pair p gives lane l the columns 32 p + 2 l
+//     and 32 p + 2 l + 1, so each state access of 16 lanes is one contiguous
+//     128-byte row segment (measured against 8 consecutive columns per lane,
+//     two 16-byte accesses at a 32-byte stride: 128 -> 113 us at B = 128,
+//     35.0 -> 31.1 us at B = 32, bitwise the same states).
 //   * Waves 2-3 sum phi over tokens for Z in fp32, one feature per thread.
 template <int D, int F, bool kResidentW>
 struct CommitGeomBf16 {
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
     using T = uint16_t;
     using P = ProjGeom<T, D, F>;
     using G = CommitGeomBf16<D, F, kResidentW>;
-    constexpr int NE = D / 16;          // N-tiles; lane owns NE consecutive columns
+    constexpr int NE = D / 16;          // N-tiles, paired: lane owns columns 32 p + 2 l, + 1
     constexpr int FW = F / 4;           // state rows per wave (this half has F rows)
     constexpr int MT = FW / 16;         // M-tiles per wave
     constexpr int NT = F / 16;
@@ -301,7 +304,9 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const int col = 8 * bc + c;
-                const int rho = (col % NE) * 16 + col / NE;   // N-tile col%NE, lane col/NE
+                // N-tile 2 (col / 32) + col % 2, lane (col % 32) / 2: lane l holds
+                // columns 32 p + 2 l, + 1 of tile pair p (128-byte row segments)
+                const int rho = (2 * (col >> 5) + (col & 1)) * 16 + ((col & 31) >> 1);
                 const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
                 uint32_t w[4];
 #pragma unroll
@@ -313,7 +318,8 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
     };
 
     // the old state goes straight into the accumulators: row
-    // f_base + 16 mt + 4 lg + r of this half, columns NE li .. NE li + NE - 1.
+    // f_base + 16 mt + 4 lg + r of this half, columns 32 q + 2 li (+ 1) of
+    // N-tiles 2q (2q + 1).
     // Multi-chunk commits load it at entry; a one-block commit loads it once
     // phi is in LDS, so the accumulators are not live during the prologue.
     floatx4 acc[MT][NE];
@@ -322,14 +328,12 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float *p = Sg + (int64_t)(f_base + 16 * mt + 4 * lg + r) * D + NE * li;
+                const float *p = Sg + (int64_t)(f_base + 16 * mt + 4 * lg + r) * D + 2 * li;
 #pragma unroll
-                for (int q = 0; q < NE / 4; ++q) {
-                    const floatx4 t = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p) + q);
-                    acc[mt][4 * q + 0][r] = t[0];
-                    acc[mt][4 * q + 1][r] = t[1];
-                    acc[mt][4 * q + 2][r] = t[2];
-                    acc[mt][4 * q + 3][r] = t[3];
+                for (int q = 0; q < NE / 2; ++q) {
+                    const floatx2 t = __builtin_nontemporal_load(reinterpret_cast<const floatx2 *>(p + 32 * q));
+                    acc[mt][2 * q + 0][r] = t[0];
+                    acc[mt][2 * q + 1][r] = t[1];
                 }
             }
     };
@@ -407,12 +411,11 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float *p = Sg + (int64_t)(f_base + 16 * mt + 4 * lg + r) * D + NE * li;
+            float *p = Sg + (int64_t)(f_base + 16 * mt + 4 * lg + r) * D + 2 * li;
 #pragma unroll
-            for (int q = 0; q < NE / 4; ++q)
-                __builtin_nontemporal_store(floatx4{acc[mt][4 * q + 0][r], acc[mt][4 * q + 1][r],
-                                                    acc[mt][4 * q + 2][r], acc[mt][4 * q + 3][r]},
-                                            reinterpret_cast<floatx4 *>(p) + q);
+            for (int q = 0; q < NE / 2; ++q)
+                __builtin_nontemporal_store(floatx2{acc[mt][2 * q + 0][r], acc[mt][2 * q + 1][r]},
+                                            reinterpret_cast<floatx2 *>(p + 32 * q));
         }
     if (zf >= 0 && zf < F) __builtin_nontemporal_store(zacc, Zg + zf);
 }
