@@ -199,6 +199,16 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_kernel(Trans
         stage_cols_f32<T, TLD>(vg + t0 * D, L, vT, tid);
         stage_colsT_f32<P2, TLD>(pqg + t0 * P2, L, phqT, tid);
         stage_colsT_f32<P2, TLD>(pkg + t0 * P2, L, phkT, tid);
+        // this lane's teacher outputs (rows 16 rt + 4 lg + r, column c0 + li),
+        // requested with the staging so their latency is not exposed later
+        float tv[2][4];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * rt + 4 * lg + r;
+                tv[rt][r] = row < L ? tg[(t0 + row) * D + c0 + li] : 0.f;
+            }
         __syncthreads();
         if (wave < 4) {
             // scores of query tile it against key tile jt, in log2 units; keys >= L masked
@@ -275,7 +285,7 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_kernel(Trans
                 o[rt][r] = ov;
                 float g = 0.f;
                 if (row < L) {
-                    const float e = ov - tg[(t0 + row) * D + c0 + li];
+                    const float e = ov - tv[rt][r];
                     loss += e * e;
                     g = 2.f * e;
                     if (a.out) a.out[(bh * N + t0 + row) * D + c0 + li] = ov;
