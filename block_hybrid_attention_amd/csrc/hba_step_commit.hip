@@ -124,6 +124,14 @@ __global__ __launch_bounds__(kFusedThreads, 2) void step_commit_kernel_bf16(Step
 #pragma unroll
     for (int c = 0; c < RING; ++c) load_chunk(c);
     const float lw2 = a.gate ? __log2f(a.gate[h]) : 0.f;   // log2 w
+    // block values of keys 8 lg + t, columns c0 and c0 + 1, requested with
+    // the other small inputs: the first chunk's dS needs them
+    uint32_t vw[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int j = 8 * lg + t;
+        vw[t] = *reinterpret_cast<const uint32_t *>(vg + (j < L ? j : L - 1) * D + c0);
+    }
 
     if (wave < 4) {
         store_rows<T, D, F>(qc, qs);
@@ -302,12 +310,6 @@ __global__ __launch_bounds__(kFusedThreads, 2) void step_commit_kernel_bf16(Step
     // their weights and phi are exactly 0)
     bf16x8 bv[2];
     {
-        uint32_t vw[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int j = 8 * lg + t;
-            vw[t] = *reinterpret_cast<const uint32_t *>(vg + (j < L ? j : L - 1) * D + c0);
-        }
         uint32_t p0[4], p1[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
