@@ -60,3 +60,49 @@ def test_graph_replay_matches_eager(dtype):
     err = row_rel(out, want)
     report(f"graph replay vs oracle {dtype}", out=err)
     assert err <= TOL[dtype]
+
+
+def test_graph_fused_commit_and_split_comparator():
+    """hba_step_commit and the key-split comparator (two kernels and a
+    caller-owned workspace) captured together; every replay bitwise equal to
+    the eager sequence."""
+    B, H, L, d, F, P = 4, 4, 32, 128, 128, 700
+    dtype = torch.bfloat16
+    g = wl.generator(8200, DEV)
+    W = wl.feature_weights(H, d, F, dtype, g, DEV)
+    blocks = [wl.block_qkv(B, H, L, d, dtype, g, DEV) for _ in range(2)]
+    Kc, Vc = (wl.normal((B, H, P, d), 1, dtype, g, DEV) for _ in range(2))
+    plen = torch.tensor([P, 0, 333, 64], dtype=torch.int32, device=DEV)
+    S = torch.zeros((B, H, 2 * F, d), device=DEV)
+    Z = torch.zeros((B, H, 2 * F), device=DEV)
+    out = torch.empty((B, H, L, d), device=DEV)
+    out_c = torch.empty((B, H, L, d), device=DEV)
+    ns = 3
+    ws = torch.empty(hba.prefix_softmax_workspace_bytes(B, H, L, d, ns) // 4, device=DEV)
+
+    def seq():
+        hba.step(*blocks[0], W, S, Z, out=out)
+        hba.step_commit(*blocks[1], W, S, Z, out=out)
+        hba.prefix_softmax(*blocks[1], Kc, Vc, prefix_len=plen, out=out_c, n_split=ns, workspace=ws)
+
+    refs = []
+    for _ in range(3):
+        seq()
+        torch.cuda.synchronize()
+        refs.append((S.clone(), Z.clone(), out.clone(), out_c.clone()))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        seq()
+    S.zero_()
+    Z.zero_()
+    torch.cuda.synchronize()
+    for r in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want, name in zip((S, Z, out, out_c), refs[r], ("S", "Z", "out", "comparator")):
+            assert torch.equal(got, want), f"replay {r}: {name} differs from the eager sequence"
+        _ = float(out_c.abs().sum())   # eager work between replays
+    ref = oracle.prefix_softmax(*blocks[1], Kc, Vc, prefix_len=plen)
+    err = row_rel(out_c, ref)
+    report("graph split comparator vs oracle", out=err)
+    assert err <= TOL[dtype]
