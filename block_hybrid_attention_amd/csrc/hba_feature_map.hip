@@ -68,9 +68,8 @@ struct FmGeomBf16 {
     static constexpr int phi_off = P::w_bytes;
     static constexpr int bytes = P::w_bytes + kRows * PLD * 4;
 };
-constexpr int kFmTiles = 4;   // 32-row tiles per workgroup
-
-template <int D, int F>
+// kFmTiles: 32-row tiles per workgroup (W^T is staged once per workgroup)
+template <int D, int F, int kFmTiles>
 __global__ __launch_bounds__(kThreads, 2) void feature_map_kernel_bf16(FeatureMapArgs a) {
     using T = uint16_t;
     using P = ProjGeom<T, D, F>;
@@ -176,8 +175,21 @@ template <typename T, int D, int F>
 static hipError_t launch_fm_t(const FeatureMapArgs &a, unsigned batches, hipStream_t stream) {
     const int64_t tiles = (a.n + kRows - 1) / kRows;
     if constexpr (sizeof(T) == 2) {
-        const unsigned groups = (unsigned)((tiles + kFmTiles - 1) / kFmTiles);
-        return launch_kernel(feature_map_kernel_bf16<D, F>, dim3(groups, (unsigned)a.H, batches), dim3(kThreads), a, stream);
+        // the most tiles per workgroup (fewest W stagings) that still launches
+        // one full round of two workgroups per CU (measured at 16 heads: 1
+        // tile best at 1024 rows, 4 at 4096, 8 at 32768)
+        const int64_t cus = device_cus();
+        const int64_t round = 2 * (cus > 0 ? cus : 256);
+        const int64_t per_tile_groups = tiles * a.H * batches;
+        const dim3 blk(kThreads);
+        auto groups = [&](int kt) { return (unsigned)((tiles + kt - 1) / kt); };
+        if (per_tile_groups >= 8 * round)
+            return launch_kernel(feature_map_kernel_bf16<D, F, 8>, dim3(groups(8), (unsigned)a.H, batches), blk, a, stream);
+        if (per_tile_groups >= 4 * round)
+            return launch_kernel(feature_map_kernel_bf16<D, F, 4>, dim3(groups(4), (unsigned)a.H, batches), blk, a, stream);
+        if (per_tile_groups >= 2 * round)
+            return launch_kernel(feature_map_kernel_bf16<D, F, 2>, dim3(groups(2), (unsigned)a.H, batches), blk, a, stream);
+        return launch_kernel(feature_map_kernel_bf16<D, F, 1>, dim3(groups(1), (unsigned)a.H, batches), blk, a, stream);
     } else {
         return launch_kernel(feature_map_kernel<T, D, F>, dim3((unsigned)tiles, (unsigned)a.H, batches), dim3(kThreads), a, stream);
     }
