@@ -246,7 +246,8 @@ int64_t hba_prefix_softmax_workspace_bytes(const hba_shape *shape, int32_t n_spl
  * the same inputs give bitwise-equal results.  batch = 0 or n_blocks = 0
  * writes zeros.
  * Errors: HBA_ERR_UNSUPPORTED for head_dim != 128; HBA_ERR_CAPACITY for a
- * workspace that is too small; otherwise as hba_step. */
+ * workspace that is too small; HBA_ERR_SHAPE for batch > 65535; otherwise
+ * as hba_step. */
 hba_status hba_transfer(const hba_shape *shape, int32_t n_blocks, const void *q, const void *k,
                         const void *v, const void *W, const float *alpha, const float *target, float *out,
                         float *loss, float *dW, float *dalpha, float *workspace, int64_t workspace_bytes,

@@ -225,6 +225,7 @@ def test_transfer_validation():
     assert call(sh, wsb=need - 4) == ECAP
     assert call(sh, W=MIS) == EALIGN
     assert call(sh, target=MIS) == EALIGN
+    assert call(shape(batch=65536, slots=1 << 17)) == ESHAPE
 
 
 def test_python_binding_refuses_host_tensors():
