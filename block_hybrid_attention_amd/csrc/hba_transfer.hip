@@ -50,7 +50,7 @@ constexpr int kXferD = 128;
 
 // Scheduling fence inside the long MFMA loops: keeps the compiler from
 // hoisting every operand load of a loop at once, which would need more
-// registers than the state, W and the accumulators leave free.
+// registers than the state and the accumulators leave free.
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
 template <int F>
@@ -62,13 +62,15 @@ struct XferGeom {
     static constexpr int vT_f = D * TLD;
     static constexpr int ph_f = P2 * TLD;
     static constexpr int pm_f = kRows * TLD;
-    static constexpr int red_f = 4 * 2 * 8 * kRows;   // [kind][x][column tile][row]
+    static constexpr int red_f = 8 * kRows;           // [wave][row] partial sums
     // forward sweep
     static constexpr int f_xq = 0, f_xk = f_xq + x_f, f_vT = f_xk + x_f, f_phq = f_vT + vT_f,
                          f_phk = f_phq + ph_f, f_pm = f_phk + ph_f, f_z = f_pm + pm_f, f_red = f_z + P2,
                          f_row = f_red + red_f, f_sc = f_row + 8 * kRows * 2, f_total = f_sc + kRows * 8;
     // gradient sweeps
-    static constexpr int s_xq = 0, s_xk = s_xq + x_f, s_vT = s_xk + x_f, s_dnT = s_vT + vT_f,
+    // a gradient sweep stages only the side whose gradient it takes, so the
+    // q and k tiles share one region
+    static constexpr int s_xq = 0, s_xk = 0, s_vT = x_f, s_dnT = s_vT + vT_f,
                          s_phq = s_dnT + vT_f, s_phk = s_phq + ph_f, s_z = s_phk + ph_f, s_dd = s_z + P2,
                          s_red = s_dd + kRows, s_total = s_red + red_f;
 };
