@@ -21,8 +21,9 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhba.so")
 ARCH = "gfx950"
 SOURCES = ["hba_api.cpp", "hba_feature_map.hip", "hba_step.hip", "hba_commit.hip",
-           "hba_prefix_softmax.hip", "hba_step_commit.hip", "hba_transfer.hip"]
-HEADERS = ["hba_device.h", "hba_internal.h"]
+           "hba_prefix_softmax.hip", "hba_step_commit.hip", "hba_transfer.hip",
+           "hba_transfer_bf16.hip"]
+HEADERS = ["hba_device.h", "hba_internal.h", "hba_transfer.h"]
 
 
 def hipcc() -> str:

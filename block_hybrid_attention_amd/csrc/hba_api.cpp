@@ -211,7 +211,8 @@ hba_status hba_transfer(const hba_shape *shape, int32_t n_blocks, const void *q,
     const int G = kv_group(shape);
     if (n_blocks < 0 || G == 0) return HBA_ERR_SHAPE;
     const int64_t N = (int64_t)n_blocks * shape->block;
-    if (N > 0x7fffffff || (int64_t)shape->batch * shape->heads * N > ((int64_t)1 << 40)) return HBA_ERR_SHAPE;
+    // one sequence (N x 128 elements per request and head) is indexed in 32 bits
+    if (N * 128 > 0x7fffffff || (int64_t)shape->batch * shape->heads * N > ((int64_t)1 << 40)) return HBA_ERR_SHAPE;
     if (shape->batch > 65535) return HBA_ERR_SHAPE;   // the feature-map pass runs one grid layer per request
     if (!W || !alpha || !loss || !dW || !dalpha || !workspace) return HBA_ERR_NULL;
     const bool work = shape->batch > 0 && n_blocks > 0;

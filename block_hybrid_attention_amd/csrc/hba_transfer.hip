@@ -42,16 +42,9 @@
 // 64 lanes of an operand read on 64 different banks.
 #include "hba_device.h"
 #include "hba_internal.h"
+#include "hba_transfer.h"
 
 namespace hba {
-
-constexpr int kXferThreads = 512;   // eight waves
-constexpr int kXferD = 128;
-
-// Scheduling fence inside the long MFMA loops: keeps the compiler from
-// hoisting every operand load of a loop at once, which would need more
-// registers than the state and the accumulators leave free.
-__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
 template <int F>
 struct XferGeom {
@@ -74,26 +67,6 @@ struct XferGeom {
                          s_phq = s_dnT + vT_f, s_phk = s_phq + ph_f, s_z = s_phk + ph_f, s_dd = s_z + P2,
                          s_red = s_dd + kRows, s_total = s_red + red_f;
 };
-
-// Workspace layout (floats), per (request, head) pair bh of BH:
-//   dnum [BH][N][d], dden [BH][Npad], phq, phk [BH][N][2F] (phi(q), phi(k)
-//   from the forward sweep), dWq [BH][d][F], dWk [BH][d][F], scal [BH][4]
-struct XferWs {
-    int64_t dnum, dden, phq, phk, dWq, dWk, scal, total;
-};
-__host__ __device__ inline XferWs xfer_ws(int64_t BH, int64_t N, int F) {
-    const int64_t npad = (N + 3) & ~int64_t(3);
-    XferWs w;
-    w.dnum = 0;
-    w.dden = w.dnum + BH * N * kXferD;
-    w.phq = w.dden + BH * npad;
-    w.phk = w.phq + BH * N * 2 * F;
-    w.dWq = w.phk + BH * N * 2 * F;
-    w.dWk = w.dWq + BH * kXferD * F;
-    w.scal = w.dWk + BH * kXferD * F;
-    w.total = w.scal + BH * 4;
-    return w;
-}
 
 int64_t transfer_workspace_floats(int64_t BH, int64_t N, int F) { return xfer_ws(BH, N, F).total; }
 
@@ -588,7 +561,12 @@ static hipError_t launch_transfer_t(const TransferArgs &a, hipStream_t stream) {
         e = launch_feature_map(fq, bf16, (int)D, F, stream, a.B);
         if (e == hipSuccess) e = launch_feature_map(fk, bf16, (int)D, F, stream, a.B);
         const dim3 grid((unsigned)pairs), block(kXferThreads);
-        if (e == hipSuccess) e = launch_kernel(transfer_forward_kernel<T, F>, grid, block, a, stream);
+        if (e == hipSuccess) {
+            if constexpr (bf16)
+                e = launch_transfer_forward_bf16(a, F, stream);
+            else
+                e = launch_kernel(transfer_forward_kernel<T, F>, grid, block, a, stream);
+        }
         if (e == hipSuccess) e = launch_kernel(transfer_sweep_kernel<T, F, false>, grid, block, a, stream);
         if (e == hipSuccess) e = launch_kernel(transfer_sweep_kernel<T, F, true>, grid, block, a, stream);
     }

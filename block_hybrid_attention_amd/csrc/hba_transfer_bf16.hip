@@ -1,0 +1,471 @@
+// hba_transfer_bf16.hip -- stage-1 attention transfer, bf16 inputs.
+//
+// Same quantities as the fp32 path in hba_transfer.hip ("Retrofitting Linear
+// Attention into Diffusion Language Models", section 3.2, over the layer of
+// section 3.1): per (request, head) one workgroup of eight waves sweeps the
+// blocks of the sequence and keeps the state in registers.  What differs:
+//   - phi(q) and phi(k) are computed inside the sweep, per block, on bf16
+//     MFMA (products of bf16 values are exact in fp32) from W^T staged once;
+//     nothing reads phi from memory.
+//   - Every product with an fp32 operand runs on v_mfma_f32_16x16x32_bf16
+//     with that operand split into a bf16 high part and a bf16 residual
+//     (x = hi + lo + O(2^-17 |x|)): hi*hi + hi*lo + lo*hi for two fp32
+//     operands, hi*b + lo*b when the other operand is an exact bf16 input.
+//     Accumulation is fp32.
+//   - The next block's q, k, v rows and teacher outputs are requested while
+//     the current block computes, so their latency is covered.
+//
+// Operand layouts of the 16x16x32 MFMA: lane l supplies A[l%16][8(l/16) + e]
+// and B[8(l/16) + e][l%16], e = 0..7; the result lands as D[4(l/16) + r][l%16].
+// The contraction index may be permuted freely as long as A and B agree.  A
+// state held in result layout (rows 16t + 4(l/16) + r of tile t) serves as a
+// B operand over pairs of tiles (2m, 2m+1) with the permutation
+//   slot e of lane group g  <->  row 32m + 16(e/4) + 4g + e%4,
+// and the phi(q) rows are stored in LDS in that order, so the matching A
+// operand is one 16-byte read.
+#include "hba_device.h"
+#include "hba_internal.h"
+#include "hba_transfer.h"
+
+namespace hba {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int F>
+struct XbGeom {
+    static constexpr int D = kXferD, P2 = 2 * F, NFT = F / 16, NPT = P2 / 16;
+    static constexpr int XLD = ProjGeom<uint16_t, kXferD, F>::XLD;   // bf16 row tiles [32][XLD]
+    static constexpr int WLD = ProjGeom<uint16_t, kXferD, F>::WLD;   // W^T [F][WLD]
+    // bf16 tiles with the token index contiguous, [column][TLD]: 80-byte rows
+    // put the 16 lanes of a 16-byte read on 16 disjoint groups of 4 banks
+    static constexpr int TLD = kRows + 8;
+    static constexpr int PQLD = P2 + 8;   // phi(q) rows [32][PQLD], permuted per 32 features
+    // byte offsets
+    static constexpr int xq = 0, xk = xq + kRows * XLD * 2, vT = xk + kRows * XLD * 2, wt = vT + D * TLD * 2,
+                         pqh = wt + F * WLD * 2, pql = pqh + kRows * PQLD * 2, pkh = pql + kRows * PQLD * 2,
+                         pkl = pkh + P2 * TLD * 2, pph = pkl + P2 * TLD * 2, ppl = pph + kRows * TLD * 2,
+                         z = ppl + kRows * TLD * 2, zp = z + P2 * 4, rs = zp + 8 * P2 * 4,
+                         rowp = rs + kRows * 4 * 4, red = rowp + 8 * kRows * 2 * 4, total = red + 16 * 4;
+    static_assert(xk % 16 == 0 && vT % 16 == 0 && wt % 16 == 0 && pqh % 16 == 0 && pql % 16 == 0 &&
+                      pkh % 16 == 0 && pkl % 16 == 0 && pph % 16 == 0 && ppl % 16 == 0 && z % 16 == 0 &&
+                      zp % 16 == 0 && rs % 16 == 0,
+                  "LDS tiles must stay 16-byte aligned");
+    static_assert(total <= 160 * 1024, "LDS budget");
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    return __builtin_bit_cast(bf16x8, u32x4{a, b, c, d});
+}
+__device__ __forceinline__ bf16x8 lds_bf16x8(const uint16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+// Four fp32 values -> bf16 high parts and residuals, written as 8 bytes each.
+__device__ __forceinline__ void store_split4(uint16_t *hi, uint16_t *lo, float v0, float v1, float v2, float v3) {
+    uint32_t h0, l0, h1, l1;
+    split_pk_bf16(v0, v1, h0, l0);
+    split_pk_bf16(v2, v3, h1, l1);
+    *reinterpret_cast<uint2 *>(hi) = make_uint2(h0, h1);
+    *reinterpret_cast<uint2 *>(lo) = make_uint2(l0, l1);
+}
+
+// The B operand of a contraction over 32 state rows: tiles 2m and 2m+1 of a
+// state held in result layout, split into high parts and residuals.
+__device__ __forceinline__ void split_state_pair(const floatx4 &s0, const floatx4 &s1, bf16x8 &hi, bf16x8 &lo) {
+    uint32_t h[4], l[4];
+    split_pk_bf16(s0[0], s0[1], h[0], l[0]);
+    split_pk_bf16(s0[2], s0[3], h[1], l[1]);
+    split_pk_bf16(s1[0], s1[1], h[2], l[2]);
+    split_pk_bf16(s1[2], s1[3], h[3], l[3]);
+    hi = as_bf16x8(h[0], h[1], h[2], h[3]);
+    lo = as_bf16x8(l[0], l[1], l[2], l[3]);
+}
+
+// One 16-byte chunk (8 bf16) of a 32-row tile per thread: row tid/16,
+// columns 8 (tid % 16) ..; rows >= nrows read as zero.  Branch-free (the
+// row is clamped, then the value zeroed), so no control flow makes loads
+// already in flight drain.
+__device__ __forceinline__ uint4 load_chunk(const uint16_t *__restrict__ rows, int nrows, int tid) {
+    const int row = tid >> 4, c0 = (tid & 15) * 8;
+    const int rr = row < nrows ? row : nrows - 1;
+    const uint4 t = *reinterpret_cast<const uint4 *>(rows + (rr * kXferD + c0));
+    const bool ok = row < nrows;
+    return make_uint4(ok ? t.x : 0u, ok ? t.y : 0u, ok ? t.z : 0u, ok ? t.w : 0u);
+}
+
+// The same chunk of v for the transposed tile vT[column][token]: row tid % 32,
+// columns 8 (tid / 32) ..  Each wave then covers all 32 rows of two column
+// chunks, so its 2-byte writes into vT land on 32 different banks.
+__device__ __forceinline__ uint4 load_chunk_t(const uint16_t *__restrict__ rows, int nrows, int tid) {
+    const int row = tid & 31, c0 = (tid >> 5) * 8;
+    const int rr = row < nrows ? row : nrows - 1;
+    const uint4 t = *reinterpret_cast<const uint4 *>(rows + (rr * kXferD + c0));
+    const bool ok = row < nrows;
+    return make_uint4(ok ? t.x : 0u, ok ? t.y : 0u, ok ? t.z : 0u, ok ? t.w : 0u);
+}
+
+// 1. Forward sweep, bf16 inputs.  Per block, after the staging barrier, each
+// wave takes one sign of phi for one 16-row tile (the projection u of that
+// tile is formed by both waves of the pair):
+//   waves 0-3  phi(q) of query tile w/2, sign w%2, its share of phi(q) . Z,
+//              phi(q) to LDS; waves 1 and 3 also the scores of their query
+//              tile against all keys, row max and sum, P to LDS;
+//   waves 4-7  phi(k) of key tile (w-4)/2, sign w%2, phi(k)^T to LDS, its
+//              partial column sums for Z.
+// Then every wave, for its 16 value columns: P V and phi(q) S, the output,
+// loss, dnum; after a barrier the commit S += phi(k)^T V, while wave 7 forms
+// each row's dden and share of dL/dw.  S [2F][d] lives in registers in
+// result layout: S[pt][r] = S[16 pt + 4(l/16) + r][16 w + l%16].
+template <int F>
+__global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_bf16_kernel(TransferArgs a) {
+    using G = XbGeom<F>;
+    constexpr int D = kXferD, P2 = G::P2, NFT = G::NFT, NPT = G::NPT;
+    constexpr int XLD = G::XLD, WLD = G::WLD, TLD = G::TLD, PQLD = G::PQLD;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[G::total];
+    uint16_t *xq = reinterpret_cast<uint16_t *>(smem + G::xq), *xk = reinterpret_cast<uint16_t *>(smem + G::xk),
+             *vT = reinterpret_cast<uint16_t *>(smem + G::vT), *wt = reinterpret_cast<uint16_t *>(smem + G::wt),
+             *pqh = reinterpret_cast<uint16_t *>(smem + G::pqh), *pql = reinterpret_cast<uint16_t *>(smem + G::pql),
+             *pkh = reinterpret_cast<uint16_t *>(smem + G::pkh), *pkl = reinterpret_cast<uint16_t *>(smem + G::pkl),
+             *pph = reinterpret_cast<uint16_t *>(smem + G::pph), *ppl = reinterpret_cast<uint16_t *>(smem + G::ppl);
+    float *Zs = reinterpret_cast<float *>(smem + G::z), *zp = reinterpret_cast<float *>(smem + G::zp),
+          *rs = reinterpret_cast<float *>(smem + G::rs), *rowp = reinterpret_cast<float *>(smem + G::rowp),
+          *red = reinterpret_cast<float *>(smem + G::red);
+
+    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int64_t bh = blockIdx.x;
+    const int h = (int)(bh % a.H);
+    const int L = a.L;
+    const int64_t N = (int64_t)a.nb * L;
+    const int64_t npad = (N + 3) & ~int64_t(3);
+    const uint16_t *qg = static_cast<const uint16_t *>(a.q) + bh * N * D;
+    const uint16_t *kg = static_cast<const uint16_t *>(a.k) + (bh / a.G) * N * D;
+    const uint16_t *vg = static_cast<const uint16_t *>(a.v) + (bh / a.G) * N * D;
+    // per-(request, head) bases (uniform); offsets inside a sequence are
+    // 32-bit: a sequence holds at most 2^31 / d elements (checked on the host)
+    const float *tg = a.target + bh * N * D;
+    float *outg = a.out ? a.out + bh * N * D : nullptr;
+    const float w = 1.f / (1.f + __expf(-a.alpha[h]));
+    const float log2w = __log2f(w);
+    constexpr float kScaleLog2 = 0.08838834764831845f * 1.4426950408889634f;   // log2(e) / sqrt(128)
+    const XferWs ws = xfer_ws((int64_t)a.B * a.H, N, F);
+    float *dng = a.ws + ws.dnum + bh * N * D;
+    float *ddg = a.ws + ws.dden + bh * npad;
+    const int c0 = 16 * wave;
+    const int lofs = 4 * lg * D + c0 + li;   // row 4 lg, column c0 + li of a block
+    {
+        WChunks<uint16_t, D, F> wc;
+        load_w<uint16_t, D, F>(static_cast<const uint16_t *>(a.W) + (int64_t)h * D * F, wc);
+        store_w<uint16_t, D, F>(wc, wt);
+    }
+    if (tid < P2) Zs[tid] = 0.f;
+    floatx4 S[NPT];
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt) S[pt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float loss = 0.f, dw = 0.f;
+
+    // block 0's inputs; later blocks are requested one block ahead
+    uint4 cq = load_chunk(qg, L, tid), ck = load_chunk(kg, L, tid), cv = load_chunk_t(vg, L, tid);
+    float tv[2][4];   // teacher outputs of rows 16 rt + 4 lg + r, column c0 + li
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * rt + 4 * lg + r;
+            tv[rt][r] = row < L ? tg[(16 * rt + r) * D + lofs] : 0.f;
+        }
+
+#pragma unroll 1
+    for (int n = 0; n < a.nb; ++n) {
+        const int t0 = n * L;
+        // The thread index, passed through an empty asm so that every address
+        // below is formed inside the loop: hoisted out of it, each access site
+        // would hold its own address register for the whole sweep instead of
+        // sharing a base with its constant offset folded into the instruction.
+        int tidv = tid;
+        asm volatile("" : "+v"(tidv));
+        const int li = tidv & 15, lg = (tidv >> 4) & 3, srow = tidv >> 4, scol = (tidv & 15) * 8;
+        const int lofs = 4 * lg * D + c0 + li;
+        *reinterpret_cast<uint4 *>(xq + srow * XLD + scol) = cq;
+        *reinterpret_cast<uint4 *>(xk + srow * XLD + scol) = ck;
+        {
+            const uint32_t vw[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                vT[((tidv >> 5) * 8 + e) * TLD + (tidv & 31)] = (uint16_t)(vw[e >> 1] >> (16 * (e & 1)));
+        }
+        if (n + 1 < a.nb) {
+            const int t1 = t0 + L;
+            cq = load_chunk(qg + t1 * D, L, tid);
+            ck = load_chunk(kg + t1 * D, L, tid);
+            cv = load_chunk_t(vg + t1 * D, L, tid);
+        }
+        __syncthreads();
+
+        if (wave < 4) {
+            // phi(q), one sign per wave: queries t = 16 rt + li, the features
+            // of sign `side` (u^T = W^T q^T, so this lane holds u[16 ft + 4 lg + r])
+            const int rt = wave >> 1, side = wave & 1, t = 16 * rt + li;
+            const float sg = side ? -1.f : 1.f;
+            floatx4 x[NFT];
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) x[ft] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+                const bf16x8 b = lds_bf16x8(xq + t * XLD + 32 * ks + 8 * lg);
+#pragma unroll
+                for (int ft = 0; ft < NFT; ++ft)
+                    x[ft] = mfma_bf16(lds_bf16x8(wt + (16 * ft + li) * WLD + 32 * ks + 8 * lg), b, x[ft]);
+                fence();
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    x[ft][r] *= sg;
+                    mx = fmaxf(mx, x[ft][r]);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+            float sum = 0.f;
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    x[ft][r] = fast_exp(x[ft][r] - mx);   // <= 1
+                    sum += x[ft][r];
+                }
+            sum += __shfl_xor(sum, 16, kWave);
+            sum += __shfl_xor(sum, 32, kWave);
+            const float inv = 1.0f / sum;
+            float lpart = 0.f;   // this sign's share of phi(q) . Z
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) {
+                const floatx4 z4 = *reinterpret_cast<const floatx4 *>(Zs + side * F + 16 * ft + 4 * lg);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    x[ft][r] *= inv;
+                    lpart += x[ft][r] * z4[r];
+                }
+                // feature 16 pt + 4 lg + r sits at 32 (pt/2) + 8 lg + 4 (pt%2) + r
+                const int pt = side * NFT + ft;
+                const int pos = t * PQLD + 32 * (pt >> 1) + 8 * lg + 4 * (pt & 1);
+                store_split4(pqh + pos, pql + pos, x[ft][0], x[ft][1], x[ft][2], x[ft][3]);
+                if ((ft & 1) == 1) fence();
+            }
+            lpart += __shfl_xor(lpart, 16, kWave);
+            lpart += __shfl_xor(lpart, 32, kWave);
+            if (lg == 0) rs[t * 4 + (side ? 3 : 0)] = lpart;
+            if (side) {
+                // scores of queries t against keys 16 jt + 4 lg + r (log2
+                // units; transposed, so this lane holds one query's keys)
+                floatx4 s[2];
+#pragma unroll
+                for (int jt = 0; jt < 2; ++jt) {
+                    s[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < D / 32; ++ks)
+                        s[jt] = mfma_bf16(lds_bf16x8(xk + (16 * jt + li) * XLD + 32 * ks + 8 * lg),
+                                          lds_bf16x8(xq + t * XLD + 32 * ks + 8 * lg), s[jt]);
+                    fence();
+                }
+                float M = -INFINITY;
+#pragma unroll
+                for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        s[jt][r] = 16 * jt + 4 * lg + r < L ? s[jt][r] * kScaleLog2 : -INFINITY;
+                        M = fmaxf(M, s[jt][r]);
+                    }
+                M = fmaxf(M, __shfl_xor(M, 16, kWave));
+                M = fmaxf(M, __shfl_xor(M, 32, kWave));   // finite: key 0 is always valid
+                float smd = 0.f;
+#pragma unroll
+                for (int jt = 0; jt < 2; ++jt) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        s[jt][r] = fast_exp2(s[jt][r] - M);
+                        smd += s[jt][r];
+                    }
+                    store_split4(pph + t * TLD + 16 * jt + 4 * lg, ppl + t * TLD + 16 * jt + 4 * lg, s[jt][0],
+                                 s[jt][1], s[jt][2], s[jt][3]);
+                }
+                smd += __shfl_xor(smd, 16, kWave);
+                smd += __shfl_xor(smd, 32, kWave);
+                if (lg == 0) {
+                    rs[t * 4 + 1] = M;
+                    rs[t * 4 + 2] = smd;
+                }
+            }
+        } else {
+            // phi(k), one sign per wave: keys 16 tt + 4 lg + r (u = k W, each
+            // key row in one DPP row of 16 lanes); rows past the block get 0
+            const int tt = (wave - 4) >> 1, side = wave & 1;
+            const float sg = side ? -1.f : 1.f;
+            floatx4 x[NFT];
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) x[ft] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+                const bf16x8 xa = lds_bf16x8(xk + (16 * tt + li) * XLD + 32 * ks + 8 * lg);
+#pragma unroll
+                for (int ft = 0; ft < NFT; ++ft)
+                    x[ft] = mfma_bf16(xa, lds_bf16x8(wt + (16 * ft + li) * WLD + 32 * ks + 8 * lg), x[ft]);
+                fence();
+            }
+            float inv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int ft = 0; ft < NFT; ++ft) {
+                    x[ft][r] *= sg;
+                    mx = fmaxf(mx, x[ft][r]);
+                }
+                mx = row16_max(mx);
+                float sum = 0.f;
+#pragma unroll
+                for (int ft = 0; ft < NFT; ++ft) {
+                    x[ft][r] = fast_exp(x[ft][r] - mx);
+                    sum += x[ft][r];
+                }
+                inv[r] = (16 * tt + 4 * lg + r < L ? 1.f : 0.f) / row16_sum(sum);
+            }
+            // phi(k)^T to LDS; this lane's four-key partial sums of each
+            // feature go to zp[4 tt + lg][f] (summed into Z after the barrier)
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[ft][r] *= inv[r];
+                const int f = side * F + 16 * ft + li;
+                store_split4(pkh + f * TLD + 16 * tt + 4 * lg, pkl + f * TLD + 16 * tt + 4 * lg, x[ft][0], x[ft][1],
+                             x[ft][2], x[ft][3]);
+                zp[(4 * tt + lg) * P2 + f] = (x[ft][0] + x[ft][1]) + (x[ft][2] + x[ft][3]);
+            }
+        }
+        __syncthreads();
+
+        // Z of blocks 0..n-1 was read above: fold block n in
+        if (tid < P2) {
+            float z = 0.f;
+#pragma unroll
+            for (int g = 0; g < 8; ++g) z += zp[g * P2 + tid];
+            Zs[tid] += z;
+        }
+        // block softmax numerator and linear readout for this wave's 16 columns
+        const bf16x8 vb = lds_bf16x8(vT + (c0 + li) * TLD + 8 * lg);
+        floatx4 smv[2], lin[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            smv[rt] = mfma_bf16(lds_bf16x8(pph + (16 * rt + li) * TLD + 8 * lg), vb, floatx4{0.f, 0.f, 0.f, 0.f});
+            smv[rt] = mfma_bf16(lds_bf16x8(ppl + (16 * rt + li) * TLD + 8 * lg), vb, smv[rt]);
+            lin[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int m = 0; m < NPT / 2; ++m) {
+            bf16x8 sh, sl;
+            split_state_pair(S[2 * m], S[2 * m + 1], sh, sl);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const int pos = (16 * rt + li) * PQLD + 32 * m + 8 * lg;
+                const bf16x8 ah = lds_bf16x8(pqh + pos), al = lds_bf16x8(pql + pos);
+                lin[rt] = mfma_bf16(ah, sh, lin[rt]);
+                lin[rt] = mfma_bf16(ah, sl, lin[rt]);
+                lin[rt] = mfma_bf16(al, sh, lin[rt]);
+            }
+            if ((m & 1) == 1) fence();
+        }
+        // output, loss, dnum = g / den, and the row sums g.o and g.smv
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * rt + 4 * lg + r;
+                // row scalars: phi(q).Z of the two signs, block max, block sum
+                const floatx4 st = *reinterpret_cast<const floatx4 *>(rs + row * 4);
+                const float lden = st[0] + st[3];
+                const float c2 = fmaxf(st[1] + log2w, __log2f(lden));
+                const float esm = fast_exp2(st[1] + log2w - c2), elin = fast_exp2(-c2);
+                const float rden = __builtin_amdgcn_rcpf(esm * st[2] + elin * lden);
+                const float ov = (esm * smv[rt][r] + elin * lin[rt][r]) * rden;
+                float g = 0.f;
+                if (row < L) {
+                    const float e = ov - tv[rt][r];
+                    loss += e * e;
+                    g = 2.f * e;
+                    const int o = (t0 + 16 * rt + r) * D + lofs;
+                    if (outg) outg[o] = ov;
+                    dng[o] = g * (elin * rden);   // elin / den = 1 / true denominator
+                }
+                const float go = row16_sum(g * ov), gs = row16_sum(g * smv[rt][r]);
+                if (li == 0) {
+                    rowp[(wave * kRows + row) * 2 + 0] = go;
+                    rowp[(wave * kRows + row) * 2 + 1] = gs;
+                }
+            }
+        if (n + 1 < a.nb) {
+            const int t1 = t0 + L;
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * rt + 4 * lg + r;
+                    tv[rt][r] = row < L ? tg[(t1 + 16 * rt + r) * D + lofs] : 0.f;
+                }
+        }
+        __syncthreads();
+
+        if (wave == 7 && lane < kRows) {
+            // per row: g.o and g.smv over the eight waves' columns, dden and
+            // the row's share of dL/dw
+            const int row = lane;
+            float go = 0.f, gs = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < 8; ++ww) {
+                go += rowp[(ww * kRows + row) * 2 + 0];
+                gs += rowp[(ww * kRows + row) * 2 + 1];
+            }
+            if (row < L) {
+                const floatx4 st = *reinterpret_cast<const floatx4 *>(rs + row * 4);
+                const float lden = st[0] + st[3];
+                const float c2 = fmaxf(st[1] + log2w, __log2f(lden));
+                const float esm = fast_exp2(st[1] + log2w - c2), elin = fast_exp2(-c2);
+                const float den = esm * st[2] + elin * lden;
+                ddg[t0 + row] = -go * (elin / den);
+                dw += (esm / w) / den * (gs - go * st[2]);
+            }
+        }
+        // commit block n: S[f][c] += sum_t phi(k_t)[f] v_t[c]
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) {
+            S[pt] = mfma_bf16(lds_bf16x8(pkh + (16 * pt + li) * TLD + 8 * lg), vb, S[pt]);
+            S[pt] = mfma_bf16(lds_bf16x8(pkl + (16 * pt + li) * TLD + 8 * lg), vb, S[pt]);
+            if ((pt & 3) == 3) fence();
+        }
+        __syncthreads();
+    }
+    loss = wave_sum(loss);
+    dw = wave_sum(dw);
+    if (lane == 0) {
+        red[wave] = loss;
+        red[8 + wave] = dw;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float s = 0.f, sw = 0.f;
+        for (int ww = 0; ww < 8; ++ww) {
+            s += red[ww];
+            sw += red[8 + ww];
+        }
+        a.ws[ws.scal + bh * 4 + 0] = s;
+        a.ws[ws.scal + bh * 4 + 1] = sw;
+    }
+}
+
+hipError_t launch_transfer_forward_bf16(const TransferArgs &a, int F, hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)a.B * a.H)), block(kXferThreads);
+    if (F == 128) return launch_kernel(transfer_forward_bf16_kernel<128>, grid, block, a, stream);
+    if (F == 64) return launch_kernel(transfer_forward_bf16_kernel<64>, grid, block, a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace hba

@@ -228,7 +228,10 @@ int64_t hba_prefix_softmax_workspace_bytes(const hba_shape *shape, int32_t n_spl
  *   dW[h]     = d loss / d W[h],   dalpha[h] = d loss / d alpha[h]
  * q, k, v and target are inputs (the backbone is frozen); the gradient flows
  * through the shared normaliser, phi(q), the states and phi(k).
- * Arithmetic is fp32 throughout (fp32 matrix cores).  head_dim 128 only.
+ * fp32 inputs run on fp32 matrix cores.  For bf16 inputs the products of
+ * two bf16 values are exact and every fp32 operand is split into a bf16 high
+ * part and a bf16 residual on the bf16 matrix cores; accumulation is fp32
+ * for both.  head_dim 128 only.
  * Reads: batch, heads, block, head_dim, feat, in_dtype, kv_heads.
  *   q, target  [B][H][N][128]      q in_dtype, target fp32
  *   k, v       [B][Hkv][N][128]    in_dtype
@@ -246,8 +249,8 @@ int64_t hba_prefix_softmax_workspace_bytes(const hba_shape *shape, int32_t n_spl
  * the same inputs give bitwise-equal results.  batch = 0 or n_blocks = 0
  * writes zeros.
  * Errors: HBA_ERR_UNSUPPORTED for head_dim != 128; HBA_ERR_CAPACITY for a
- * workspace that is too small; HBA_ERR_SHAPE for batch > 65535; otherwise
- * as hba_step. */
+ * workspace that is too small; HBA_ERR_SHAPE for batch > 65535 or
+ * N * 128 >= 2^31; otherwise as hba_step. */
 hba_status hba_transfer(const hba_shape *shape, int32_t n_blocks, const void *q, const void *k,
                         const void *v, const void *W, const float *alpha, const float *target, float *out,
                         float *loss, float *dW, float *dalpha, float *workspace, int64_t workspace_bytes,

@@ -226,6 +226,8 @@ def test_transfer_validation():
     assert call(sh, W=MIS) == EALIGN
     assert call(sh, target=MIS) == EALIGN
     assert call(shape(batch=65536, slots=1 << 17)) == ESHAPE
+    # one sequence is indexed in 32 bits: N * 128 < 2^31 (block 32 here)
+    assert call(sh, nb=(1 << 24) // 32) == ESHAPE
 
 
 def test_python_binding_refuses_host_tensors():
