@@ -179,10 +179,27 @@ def transfer_flops(d, F, L) -> int:
     return 2 * 2 * d * F + 2 * 2 * L * d + 5 * 2 * (2 * F) * d + 2 * 2 * d * F
 
 
+def transfer_mfma_bf16(F) -> int:
+    """v_mfma_f32_16x16x32_bf16 instructions the bf16 path of hba_transfer
+    issues per 32-row token tile and head (all three sweeps; fp32 operands
+    split into high and residual parts count once per part product):
+    forward: projections 32 NFT, scores 16, P V 32, linear readout 24 NPT,
+    commit 16 NPT; query sweep: projections 32 NFT, dphi 192 FW, fold 144 FW,
+    dW 32 NWT; key sweep: projections 32 NFT, dphi 128 FW, fold 216 FW,
+    dW 32 NWT (NFT = F/16, NPT = 2F/16, FW = NPT/8, NWT = F/16)."""
+    nft, npt = F // 16, 2 * F // 16
+    fw, nwt = npt // 8, F // 16
+    fwd = 32 * nft + 16 + 32 + 24 * npt + 16 * npt
+    qsw = 32 * nft + 192 * fw + 144 * fw + 32 * nwt
+    ksw = 32 * nft + 128 * fw + 216 * fw + 32 * nwt
+    return fwd + qsw + ksw
+
+
 def transfer_bench(args, torch, hba, wl, dev):
     """Stage-1 attention transfer: loss and dW, dalpha for 16 sequences of
-    2048 tokens (64 blocks of 32) x 16 heads, d = F = 128, bf16 inputs, fp32
-    arithmetic, against a synthetic teacher output."""
+    2048 tokens (64 blocks of 32) x 16 heads, d = F = 128, bf16 inputs,
+    fp32 accumulation (bf16 MFMA with split operands), against a synthetic
+    teacher output."""
     B, H, L, nb, d, F = 16, 16, 32, 64, 128, 128
     N = nb * L
     g = wl.generator(6_000_000, dev)
@@ -195,11 +212,15 @@ def transfer_bench(args, torch, hba, wl, dev):
     ms = _time_launches(torch, lambda: hba.transfer(q, k, v, W, alpha, target, L, workspace=ws), 2,
                         max(3, min(args.steps, 10)), stream)
     fl = transfer_flops(d, F, L) * B * H * N
+    issued = transfer_mfma_bf16(F) * 16 * 16 * 32 * 2 * B * H * nb
     print(json.dumps({"mode": "transfer", "batch": B, "heads": H, "tokens": N, "block": L, "head_dim": d,
-                      "feat": F, "dtype": "bf16 inputs, fp32 arithmetic (fp32 MFMA; the feature map on bf16 MFMA, exact products)", "ms": ms,
+                      "feat": F, "dtype": "bf16 inputs; bf16 MFMA, fp32 operands split into high and residual "
+                      "parts, fp32 accumulation", "ms": ms,
                       "tokens_per_s": B * N / (ms * 1e-3), "algorithmic_flops": fl,
                       "TFLOPs": fl / (ms * 1e-3) / 1e12, "fp32_mfma_peak_TFLOPs": 157.3,
-                      "frac_of_fp32_mfma_peak": fl / (ms * 1e-3) / 1e12 / 157.3}), flush=True)
+                      "frac_of_fp32_mfma_peak": fl / (ms * 1e-3) / 1e12 / 157.3,
+                      "bf16_mfma_issued_TFLOPs": issued / (ms * 1e-3) / 1e12, "bf16_mfma_peak_TFLOPs": 2500.0,
+                      "frac_of_bf16_mfma_peak": issued / (ms * 1e-3) / 1e12 / 2500.0}), flush=True)
 
 
 def decode_loop(args, torch, hba, wl, dev):

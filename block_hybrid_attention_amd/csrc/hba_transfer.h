@@ -35,7 +35,8 @@ __host__ __device__ inline XferWs xfer_ws(int64_t BH, int64_t N, int F) {
     return w;
 }
 
-// Forward sweep for bf16 inputs (hba_transfer_bf16.hip).
+// Forward sweep and the two gradient sweeps for bf16 inputs (hba_transfer_bf16.hip).
 hipError_t launch_transfer_forward_bf16(const TransferArgs &a, int F, hipStream_t stream);
+hipError_t launch_transfer_sweeps_bf16(const TransferArgs &a, int F, hipStream_t stream);
 
 }  // namespace hba

@@ -18,10 +18,11 @@
 //   du = p (dp - p.dp) - p' (dp' - p'.dp')  for phi = [p, p'] = [softmax(u), softmax(-u)],
 //   dW += x du^T for every query row and key row x.
 //
-// Six launches:
+// This file holds the fp32-input path and the launcher; bf16 inputs run the
+// kernels of hba_transfer_bf16.hip (same sweeps, phi computed inside them,
+// bf16 MFMA with split operands).  The fp32 path makes six launches:
 //   0. the feature map (hba_feature_map's kernels) of every query and key
-//      row into the workspace, fully parallel over rows; bf16 inputs run on
-//      bf16 MFMA, whose products of bf16 values are exact.  The three sweeps
+//      row into the workspace, fully parallel over rows.  The three sweeps
 //      below stage phi from there instead of computing it per block.
 // then one workgroup of eight waves per (request, head) for the three sweeps
 // over the blocks:
@@ -34,9 +35,8 @@
 //   3. key sweep, backward over the blocks: dphi(k) = v G^T + Gz, G updated
 //      after each block with phi(q)^T dnum; into dW.
 //   4. reduction of the per-(request, head) parts over requests, in request
-//      order (deterministic).
-// Every product of the sweeps runs on fp32 MFMA (v_mfma_f32_16x16x4f32), so
-// the arithmetic is fp32 throughout; bf16 inputs are widened when staged.
+//      order (deterministic; shared by both paths).
+// Every product of these sweeps runs on fp32 MFMA (v_mfma_f32_16x16x4f32).
 // Token tiles that MFMA reads with the token index on the 16-lane axis are
 // staged transposed in LDS ([column][32 tokens + 4]); that stride puts the
 // 64 lanes of an operand read on 64 different banks.
@@ -549,26 +549,26 @@ static hipError_t launch_transfer_t(const TransferArgs &a, hipStream_t stream) {
     const int64_t pairs = (int64_t)a.B * a.H;
     hipError_t e = hipSuccess;
     if (pairs > 0 && a.nb > 0) {
-        // phi(q) and phi(k) of every token first, fully parallel, into the
-        // workspace rows [B H][N][2F]; the three sweeps stage them from there
-        const int64_t N = (int64_t)a.nb * a.L, D = kXferD, P2 = 2 * F;
-        const XferWs ws = xfer_ws(pairs, N, F);
-        const FeatureMapArgs fq{a.q, a.W, a.ws + ws.phq, N, a.H, D, N * D, (int64_t)a.H * N * D,
-                                P2, N * P2, (int64_t)a.H * N * P2, 1};
-        const FeatureMapArgs fk{a.k, a.W, a.ws + ws.phk, N, a.H, D, N * D, (int64_t)(a.H / a.G) * N * D,
-                                P2, N * P2, (int64_t)a.H * N * P2, a.G};
-        constexpr bool bf16 = sizeof(T) == 2;
-        e = launch_feature_map(fq, bf16, (int)D, F, stream, a.B);
-        if (e == hipSuccess) e = launch_feature_map(fk, bf16, (int)D, F, stream, a.B);
-        const dim3 grid((unsigned)pairs), block(kXferThreads);
-        if (e == hipSuccess) {
-            if constexpr (bf16)
-                e = launch_transfer_forward_bf16(a, F, stream);
-            else
-                e = launch_kernel(transfer_forward_kernel<T, F>, grid, block, a, stream);
+        if constexpr (sizeof(T) == 2) {
+            // bf16 inputs: hba_transfer_bf16.hip, phi computed inside the sweeps
+            e = launch_transfer_forward_bf16(a, F, stream);
+            if (e == hipSuccess) e = launch_transfer_sweeps_bf16(a, F, stream);
+        } else {
+            // phi(q) and phi(k) of every token first, fully parallel, into the
+            // workspace rows [B H][N][2F]; the three sweeps stage them from there
+            const int64_t N = (int64_t)a.nb * a.L, D = kXferD, P2 = 2 * F;
+            const XferWs ws = xfer_ws(pairs, N, F);
+            const FeatureMapArgs fq{a.q, a.W, a.ws + ws.phq, N, a.H, D, N * D, (int64_t)a.H * N * D,
+                                    P2, N * P2, (int64_t)a.H * N * P2, 1};
+            const FeatureMapArgs fk{a.k, a.W, a.ws + ws.phk, N, a.H, D, N * D, (int64_t)(a.H / a.G) * N * D,
+                                    P2, N * P2, (int64_t)a.H * N * P2, a.G};
+            e = launch_feature_map(fq, false, (int)D, F, stream, a.B);
+            if (e == hipSuccess) e = launch_feature_map(fk, false, (int)D, F, stream, a.B);
+            const dim3 grid((unsigned)pairs), block(kXferThreads);
+            if (e == hipSuccess) e = launch_kernel(transfer_forward_kernel<T, F>, grid, block, a, stream);
+            if (e == hipSuccess) e = launch_kernel(transfer_sweep_kernel<T, F, false>, grid, block, a, stream);
+            if (e == hipSuccess) e = launch_kernel(transfer_sweep_kernel<T, F, true>, grid, block, a, stream);
         }
-        if (e == hipSuccess) e = launch_kernel(transfer_sweep_kernel<T, F, false>, grid, block, a, stream);
-        if (e == hipSuccess) e = launch_kernel(transfer_sweep_kernel<T, F, true>, grid, block, a, stream);
     }
     if (e != hipSuccess) return e;
     TransferArgs r = a;

@@ -461,6 +461,432 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_bf16_kernel(
     }
 }
 
+// Eight fp32 values of a 32-row tile per thread, rows >= nrows zero.
+// Row layout: row tid/16, columns 8 (tid % 16) ..; column layout (for a
+// transposed tile): row tid % 32, columns 8 (tid / 32) ..
+template <bool COLS>
+__device__ __forceinline__ void load_chunk_f32(const float *__restrict__ rows, int nrows, int tid, float4 &lo4,
+                                               float4 &hi4) {
+    const int row = COLS ? (tid & 31) : (tid >> 4), c0 = COLS ? (tid >> 5) * 8 : (tid & 15) * 8;
+    const int rr = row < nrows ? row : nrows - 1;
+    const float4 a = *reinterpret_cast<const float4 *>(rows + (rr * kXferD + c0));
+    const float4 b = *reinterpret_cast<const float4 *>(rows + (rr * kXferD + c0 + 4));
+    const bool ok = row < nrows;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    lo4 = ok ? a : z;
+    hi4 = ok ? b : z;
+}
+
+// Position of column c (a multiple of 4) of a row stored in the permuted
+// order of the state contraction: column 32m + 16h + 4g + r at 32m + 8g + 4h + r.
+__device__ __forceinline__ int perm_col4(int c) {
+    return (c & ~31) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1);
+}
+
+template <int F, bool KEYS>
+struct XsGeom {
+    static constexpr int D = kXferD, P2 = 2 * F, NPT = P2 / 16, FW = NPT / 8;
+    static constexpr int XLD = ProjGeom<uint16_t, kXferD, F>::XLD, WLD = ProjGeom<uint16_t, kXferD, F>::WLD;
+    static constexpr int TLD = kRows + 8, CLD = D + 8, PXLD = P2 + 4;
+    static constexpr int UROWS = D + 16;   // U^T rows: d value columns, then the Z / Gz row and 15 zero rows
+    static constexpr int wt = 0, xs = wt + F * WLD * 2, ys = xs + kRows * XLD * 2, xT = ys + kRows * XLD * 2,
+                         uh = xT + D * TLD * 2, ul = uh + UROWS * TLD * 2,
+                         yh = ul + (KEYS ? UROWS * TLD * 2 : 0), yl = yh + P2 * TLD * 2, px = yl + P2 * TLD * 2,
+                         dd = px + kRows * PXLD * 4, red = dd + kRows * 4, total = red + 8 * kRows * 4;
+    // the contraction operand C (dnum split, or v) is staged over the x / y
+    // row tiles once the projections have read them
+    static constexpr int cph = xs, cpl = ys;
+    static_assert(kRows * CLD * 2 <= kRows * XLD * 2, "C rows must fit a row tile");
+    static_assert(xs % 16 == 0 && ys % 16 == 0 && xT % 16 == 0 && uh % 16 == 0 && ul % 16 == 0 && yh % 16 == 0 &&
+                      yl % 16 == 0 && px % 16 == 0 && dd % 16 == 0 && red % 16 == 0,
+                  "LDS tiles must stay 16-byte aligned");
+    static_assert(total <= 160 * 1024, "LDS budget");
+};
+
+// 2./3. Gradient sweeps, bf16 inputs.  KEYS = false: x = q, blocks in order,
+//   state S (phi(k)^T v, with Z as an extra value column), y = k, U = v,
+//   dphi(q) = dnum S^T + dden Z.
+// KEYS = true: x = k, blocks in reverse, state G (phi(q)^T dnum, with Gz as
+//   an extra column fed by dden), y = q, U = dnum,
+//   dphi(k) = v G^T + Gz for the block's keys.
+// The state X^T [d + 16][2F] lives in registers split by feature: wave w
+// holds features fw0 .. fw0 + 16 FW - 1 (fw0 = 16 FW w) for every value
+// column, X[a][b][r] = X^T[16 a + 4(l/16) + r][fw0 + 16 b + l%16]; in that
+// layout it is directly the B operand of the contraction over value columns.
+// Per block, with a barrier after each step:
+//   A  stage x and y rows, x^T, U^T (and dden);
+//   B  waves 0-3 phi(x) (one 16-row tile and one sign each, fp32 rows to LDS),
+//      waves 4-7 phi(y) (phi(y)^T split to LDS, rows past the block zero);
+//   C  stage C over the row tiles, permuted for the state contraction;
+//   D  dphi = C X^T (+ the Z / Gz term), then fold the block into X, and each
+//      row's p . dphi over the wave's features;
+//   E  du = +-p (dphi - p . dphi over the sign's features) into LDS (du^T,
+//      over phi(y)^T);
+//   F  dW^T += du^T x for the wave's dW tiles (both signs of each feature).
+template <int F, bool KEYS>
+__global__ __launch_bounds__(kXferThreads, 1) void transfer_sweep_bf16_kernel(TransferArgs a) {
+    using G = XsGeom<F, KEYS>;
+    constexpr int D = kXferD, P2 = G::P2, NFT = F / 16, FW = G::FW, NA = D / 16 + 1;
+    constexpr int XLD = G::XLD, WLD = G::WLD, TLD = G::TLD, CLD = G::CLD, PXLD = G::PXLD;
+    constexpr int NWT = F == 128 ? 8 : 4;   // dW tiles per wave
+    __shared__ __attribute__((aligned(16))) unsigned char smem[G::total];
+    uint16_t *wt = reinterpret_cast<uint16_t *>(smem + G::wt), *xs = reinterpret_cast<uint16_t *>(smem + G::xs),
+             *ys = reinterpret_cast<uint16_t *>(smem + G::ys), *xT = reinterpret_cast<uint16_t *>(smem + G::xT),
+             *uh = reinterpret_cast<uint16_t *>(smem + G::uh), *ul = reinterpret_cast<uint16_t *>(smem + G::ul),
+             *yh = reinterpret_cast<uint16_t *>(smem + G::yh), *yl = reinterpret_cast<uint16_t *>(smem + G::yl),
+             *cph = reinterpret_cast<uint16_t *>(smem + G::cph), *cpl = reinterpret_cast<uint16_t *>(smem + G::cpl);
+    float *px = reinterpret_cast<float *>(smem + G::px), *dd = reinterpret_cast<float *>(smem + G::dd),
+          *red = reinterpret_cast<float *>(smem + G::red);
+
+    const int tid = (int)threadIdx.x, wave = tid >> 6;
+    const int64_t bh = blockIdx.x;
+    const int h = (int)(bh % a.H);
+    const int L = a.L;
+    const int64_t N = (int64_t)a.nb * L;
+    const int64_t npad = (N + 3) & ~int64_t(3);
+    const uint16_t *qg = static_cast<const uint16_t *>(a.q) + bh * N * D;
+    const uint16_t *kg = static_cast<const uint16_t *>(a.k) + (bh / a.G) * N * D;
+    const uint16_t *vg = static_cast<const uint16_t *>(a.v) + (bh / a.G) * N * D;
+    const uint16_t *xg = KEYS ? kg : qg;   // the side whose gradient this sweep takes
+    const uint16_t *yg = KEYS ? qg : kg;   // the side folded into the state
+    const XferWs ws = xfer_ws((int64_t)a.B * a.H, N, F);
+    const float *dng = a.ws + ws.dnum + bh * N * D;
+    const float *ddg = a.ws + ws.dden + bh * npad;
+    const int fw0 = 16 * FW * wave;
+    const int wft = F == 128 ? wave : (wave & 3);           // dW feature tile
+    const int wkd0 = F == 128 ? 0 : 4 * (wave >> 2);        // first dW value tile
+
+    {
+        WChunks<uint16_t, D, F> wc;
+        load_w<uint16_t, D, F>(static_cast<const uint16_t *>(a.W) + (int64_t)h * D * F, wc);
+        store_w<uint16_t, D, F>(wc, wt);
+    }
+    // U^T rows d .. d+15: row d is 1 for the block's tokens (queries: Z
+    // counts phi(k)) or dden (keys: written per block); the rest stay 0
+    for (int e = tid; e < 16 * TLD; e += kXferThreads) {
+        const int row = e / TLD, col = e % TLD;
+        uh[(D + row) * TLD + col] = (!KEYS && row == 0 && col < L) ? (uint16_t)0x3F80 : (uint16_t)0;
+        if (KEYS) ul[(D + row) * TLD + col] = 0;
+    }
+    floatx4 X[NA][FW];
+#pragma unroll
+    for (int c = 0; c < NA; ++c)
+#pragma unroll
+        for (int b = 0; b < FW; ++b) X[c][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+    floatx4 dWa[NWT];
+#pragma unroll
+    for (int m = 0; m < NWT; ++m) dWa[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    auto block_row = [&](int it) { return (KEYS ? a.nb - 1 - it : it) * L; };
+    uint4 cx, cy, cxt, cv;
+    float4 cd0, cd1;
+    float cdd = 0.f;
+    auto request = [&](int it) {
+        const int t0 = block_row(it);
+        cx = load_chunk(xg + t0 * D, L, tid);
+        cy = load_chunk(yg + t0 * D, L, tid);
+        cxt = load_chunk_t(xg + t0 * D, L, tid);
+        cv = KEYS ? load_chunk(vg + t0 * D, L, tid) : load_chunk_t(vg + t0 * D, L, tid);
+        load_chunk_f32<KEYS>(dng + t0 * D, L, tid, cd0, cd1);
+        if (tid < kRows) cdd = tid < L ? ddg[t0 + tid] : 0.f;
+    };
+    request(0);
+
+#pragma unroll 1
+    for (int it_ = 0; it_ < a.nb; ++it_) {
+        // the thread index through an empty asm: addresses are formed inside
+        // the loop, sharing bases with their constant offsets folded
+        int tidv = tid;
+        asm volatile("" : "+v"(tidv));
+        const int li = tidv & 15, lg = (tidv >> 4) & 3;
+        const int srow = tidv >> 4, scol = (tidv & 15) * 8;     // row-layout chunk
+        const int trow = tidv & 31, tcol = (tidv >> 5) * 8;     // column-layout chunk
+
+        // A. stage
+        *reinterpret_cast<uint4 *>(xs + srow * XLD + scol) = cx;
+        *reinterpret_cast<uint4 *>(ys + srow * XLD + scol) = cy;
+        {
+            const uint32_t w4[4] = {cxt.x, cxt.y, cxt.z, cxt.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xT[(tcol + e) * TLD + trow] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+        }
+        if constexpr (!KEYS) {
+            const uint32_t w4[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) uh[(tcol + e) * TLD + trow] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+            if (tidv < kRows) dd[tidv] = cdd;
+        } else {
+            // dnum^T split into high parts and residuals, dden as row d
+            const float d8[8] = {cd0.x, cd0.y, cd0.z, cd0.w, cd1.x, cd1.y, cd1.z, cd1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const __bf16 hi = (__bf16)d8[e];
+                const __bf16 lo = (__bf16)(d8[e] - (float)hi);
+                uh[(tcol + e) * TLD + trow] = __builtin_bit_cast(uint16_t, hi);
+                ul[(tcol + e) * TLD + trow] = __builtin_bit_cast(uint16_t, lo);
+            }
+            if (tidv < kRows) {
+                const __bf16 hi = (__bf16)cdd;
+                const __bf16 lo = (__bf16)(cdd - (float)hi);
+                uh[D * TLD + tidv] = __builtin_bit_cast(uint16_t, hi);
+                ul[D * TLD + tidv] = __builtin_bit_cast(uint16_t, lo);
+            }
+        }
+        // the contraction operand waits in registers until phase C
+        const uint4 cvc = cv;
+        const float4 cdc0 = cd0, cdc1 = cd1;
+        if (it_ + 1 < a.nb) request(it_ + 1);
+        __syncthreads();
+
+        // B. feature maps of both sides
+        if (wave < 4) {
+            // phi(x) rows t = 16 rt + li, one sign per wave (lane holds u[16 ft + 4 lg + r])
+            const int rt = wave >> 1, side = wave & 1, t = 16 * rt + li;
+            const float sg = side ? -1.f : 1.f;
+            floatx4 x[NFT];
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) x[ft] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+                const bf16x8 b = lds_bf16x8(xs + t * XLD + 32 * ks + 8 * lg);
+#pragma unroll
+                for (int ft = 0; ft < NFT; ++ft)
+                    x[ft] = mfma_bf16(lds_bf16x8(wt + (16 * ft + li) * WLD + 32 * ks + 8 * lg), b, x[ft]);
+                fence();
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    x[ft][r] *= sg;
+                    mx = fmaxf(mx, x[ft][r]);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+            float sum = 0.f;
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    x[ft][r] = fast_exp(x[ft][r] - mx);
+                    sum += x[ft][r];
+                }
+            sum += __shfl_xor(sum, 16, kWave);
+            sum += __shfl_xor(sum, 32, kWave);
+            const float inv = 1.0f / sum;
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[ft][r] *= inv;
+                *reinterpret_cast<floatx4 *>(px + t * PXLD + side * F + 16 * ft + 4 * lg) = x[ft];
+            }
+        } else {
+            // phi(y) rows 16 tt + 4 lg + r, one sign per wave; rows past the block get 0
+            const int tt = (wave - 4) >> 1, side = wave & 1;
+            const float sg = side ? -1.f : 1.f;
+            floatx4 x[NFT];
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) x[ft] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+                const bf16x8 xa = lds_bf16x8(ys + (16 * tt + li) * XLD + 32 * ks + 8 * lg);
+#pragma unroll
+                for (int ft = 0; ft < NFT; ++ft)
+                    x[ft] = mfma_bf16(xa, lds_bf16x8(wt + (16 * ft + li) * WLD + 32 * ks + 8 * lg), x[ft]);
+                fence();
+            }
+            float inv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int ft = 0; ft < NFT; ++ft) {
+                    x[ft][r] *= sg;
+                    mx = fmaxf(mx, x[ft][r]);
+                }
+                mx = row16_max(mx);
+                float sum = 0.f;
+#pragma unroll
+                for (int ft = 0; ft < NFT; ++ft) {
+                    x[ft][r] = fast_exp(x[ft][r] - mx);
+                    sum += x[ft][r];
+                }
+                inv[r] = (16 * tt + 4 * lg + r < L ? 1.f : 0.f) / row16_sum(sum);
+            }
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[ft][r] *= inv[r];
+                const int f = side * F + 16 * ft + li;
+                store_split4(yh + f * TLD + 16 * tt + 4 * lg, yl + f * TLD + 16 * tt + 4 * lg, x[ft][0], x[ft][1],
+                             x[ft][2], x[ft][3]);
+            }
+        }
+        __syncthreads();
+
+        // C. the contraction operand over the row tiles, columns permuted
+        if constexpr (!KEYS) {
+            const float d8[8] = {cdc0.x, cdc0.y, cdc0.z, cdc0.w, cdc1.x, cdc1.y, cdc1.z, cdc1.w};
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int pos = srow * CLD + perm_col4(scol + 4 * hh);
+                store_split4(cph + pos, cpl + pos, d8[4 * hh], d8[4 * hh + 1], d8[4 * hh + 2], d8[4 * hh + 3]);
+            }
+        } else {
+            *reinterpret_cast<uint2 *>(cph + srow * CLD + perm_col4(scol)) = make_uint2(cvc.x, cvc.y);
+            *reinterpret_cast<uint2 *>(cph + srow * CLD + perm_col4(scol + 4)) = make_uint2(cvc.z, cvc.w);
+        }
+        __syncthreads();
+
+        // D. dphi[i][f] = sum_c C[i][c] X^T[c][f] for this wave's features
+        floatx4 dp[2][FW];
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+            for (int b = 0; b < FW; ++b) dp[i2][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m) {
+            bf16x8 sh[FW], sl[FW];
+#pragma unroll
+            for (int b = 0; b < FW; ++b) split_state_pair(X[2 * m][b], X[2 * m + 1][b], sh[b], sl[b]);
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2) {
+                const int pos = (16 * i2 + li) * CLD + 32 * m + 8 * lg;
+                const bf16x8 ah = lds_bf16x8(cph + pos);
+#pragma unroll
+                for (int b = 0; b < FW; ++b) {
+                    dp[i2][b] = mfma_bf16(ah, sh[b], dp[i2][b]);
+                    dp[i2][b] = mfma_bf16(ah, sl[b], dp[i2][b]);
+                }
+                if constexpr (!KEYS) {
+                    const bf16x8 al = lds_bf16x8(cpl + pos);
+#pragma unroll
+                    for (int b = 0; b < FW; ++b) dp[i2][b] = mfma_bf16(al, sh[b], dp[i2][b]);
+                }
+            }
+            fence();
+        }
+        // + Z[f] dden_i (queries) or Gz[f] for the block's keys; Z / Gz sit in
+        // the extra value column, lane l%16 of lane group 0
+        float zf[FW];
+#pragma unroll
+        for (int b = 0; b < FW; ++b) zf[b] = __shfl(X[NA - 1][b][0], li, kWave);
+        float pv[2][FW][4];   // phi(x) at (row 16 i2 + 4 lg + r, feature fw0 + 16 b + li)
+        float part[2][4];
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * i2 + 4 * lg + r;
+                const float s = KEYS ? (row < L ? 1.f : 0.f) : dd[row];
+                float acc = 0.f;
+#pragma unroll
+                for (int b = 0; b < FW; ++b) {
+                    dp[i2][b][r] += s * zf[b];
+                    pv[i2][b][r] = px[row * PXLD + fw0 + 16 * b + li];
+                    acc += pv[i2][b][r] * dp[i2][b][r];
+                }
+                part[i2][r] = acc;
+            }
+        // fold the block into the state: X^T[c][f] += sum_t U[t][c] Y[t][f]
+        {
+            bf16x8 bh_[FW], bl_[FW];
+#pragma unroll
+            for (int b = 0; b < FW; ++b) {
+                bh_[b] = lds_bf16x8(yh + (fw0 + 16 * b + li) * TLD + 8 * lg);
+                bl_[b] = lds_bf16x8(yl + (fw0 + 16 * b + li) * TLD + 8 * lg);
+            }
+#pragma unroll
+            for (int c = 0; c < NA; ++c) {
+                const bf16x8 uah = lds_bf16x8(uh + (16 * c + li) * TLD + 8 * lg);
+#pragma unroll
+                for (int b = 0; b < FW; ++b) {
+                    X[c][b] = mfma_bf16(uah, bh_[b], X[c][b]);
+                    X[c][b] = mfma_bf16(uah, bl_[b], X[c][b]);
+                }
+                if constexpr (KEYS) {
+                    const bf16x8 ual = lds_bf16x8(ul + (16 * c + li) * TLD + 8 * lg);
+#pragma unroll
+                    for (int b = 0; b < FW; ++b) X[c][b] = mfma_bf16(ual, bh_[b], X[c][b]);
+                }
+                if ((c & 1) == 1) fence();
+            }
+        }
+        // each row's p . dphi over this wave's features
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float tot = row16_sum(part[i2][r]);
+                if (li == 0) red[wave * kRows + 16 * i2 + 4 * lg + r] = tot;
+            }
+        __syncthreads();
+
+        // E. du = +-p (dphi - p . dphi over this sign's features), into du^T
+        {
+            const int w0 = wave < 4 ? 0 : 4;
+            const float sgn = wave < 4 ? 1.f : -1.f;
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2) {
+                floatx4 du[FW];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * i2 + 4 * lg + r;
+                    const float tot = red[(w0 + 0) * kRows + row] + red[(w0 + 1) * kRows + row] +
+                                      red[(w0 + 2) * kRows + row] + red[(w0 + 3) * kRows + row];
+#pragma unroll
+                    for (int b = 0; b < FW; ++b) du[b][r] = sgn * pv[i2][b][r] * (dp[i2][b][r] - tot);
+                }
+#pragma unroll
+                for (int b = 0; b < FW; ++b) {
+                    const int f = fw0 + 16 * b + li;
+                    store_split4(yh + f * TLD + 16 * i2 + 4 * lg, yl + f * TLD + 16 * i2 + 4 * lg, du[b][0], du[b][1],
+                                 du[b][2], du[b][3]);
+                }
+            }
+        }
+        __syncthreads();
+
+        // F. dW^T[f'][kd] += sum_t (du[t][f'] + du[t][F + f']) x[t][kd]
+        {
+            const int f1 = (16 * wft + li) * TLD + 8 * lg, f2 = (F + 16 * wft + li) * TLD + 8 * lg;
+            const bf16x8 a1h = lds_bf16x8(yh + f1), a1l = lds_bf16x8(yl + f1);
+            const bf16x8 a2h = lds_bf16x8(yh + f2), a2l = lds_bf16x8(yl + f2);
+#pragma unroll
+            for (int m = 0; m < NWT; ++m) {
+                const bf16x8 xb = lds_bf16x8(xT + (16 * (wkd0 + m) + li) * TLD + 8 * lg);
+                dWa[m] = mfma_bf16(a1h, xb, dWa[m]);
+                dWa[m] = mfma_bf16(a1l, xb, dWa[m]);
+                dWa[m] = mfma_bf16(a2h, xb, dWa[m]);
+                dWa[m] = mfma_bf16(a2l, xb, dWa[m]);
+                if ((m & 3) == 3) fence();
+            }
+        }
+        __syncthreads();
+    }
+    // dW parts in the workspace layout [d][F]
+    const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
+    float *dWg = a.ws + (KEYS ? ws.dWk : ws.dWq) + bh * D * F;
+#pragma unroll
+    for (int m = 0; m < NWT; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dWg[(int64_t)(16 * (wkd0 + m) + li) * F + 16 * wft + 4 * lg + r] = dWa[m][r];
+}
+
+hipError_t launch_transfer_sweeps_bf16(const TransferArgs &a, int F, hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)a.B * a.H)), block(kXferThreads);
+    hipError_t e = hipErrorInvalidValue;
+    if (F == 128) {
+        e = launch_kernel(transfer_sweep_bf16_kernel<128, false>, grid, block, a, stream);
+        if (e == hipSuccess) e = launch_kernel(transfer_sweep_bf16_kernel<128, true>, grid, block, a, stream);
+    } else if (F == 64) {
+        e = launch_kernel(transfer_sweep_bf16_kernel<64, false>, grid, block, a, stream);
+        if (e == hipSuccess) e = launch_kernel(transfer_sweep_bf16_kernel<64, true>, grid, block, a, stream);
+    }
+    return e;
+}
+
 hipError_t launch_transfer_forward_bf16(const TransferArgs &a, int F, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)a.B * a.H)), block(kXferThreads);
     if (F == 128) return launch_kernel(transfer_forward_bf16_kernel<128>, grid, block, a, stream);

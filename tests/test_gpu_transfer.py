@@ -3,9 +3,10 @@ alpha) against the fp64 oracle on the same seeded inputs.
 
 Measures: the loss and each head's dW by relative error (Frobenius norm for
 dW), dalpha by its error relative to the norm of the dalpha vector, the
-layer output by the usual per-row relative error.  The arithmetic is fp32 for
-both input dtypes (bf16 inputs are exact in fp32); the forward values meet
-the fp32 bar for both, the gradients the bar of their input dtype."""
+layer output by the usual per-row relative error.  fp32 inputs run on fp32
+matrix cores; bf16 inputs on bf16 matrix cores with fp32 operands split into
+high and residual parts and fp32 accumulation.  The forward values meet the
+fp32 bar for both, the gradients the bar of their input dtype."""
 import numpy as np
 import pytest
 import torch
