@@ -54,7 +54,8 @@ def errors(got, ref):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("F", [128, 64])
-@pytest.mark.parametrize("L,nb,Hkv", [(32, 4, 2), (7, 5, 1), (32, 1, 2), (19, 3, 2)])
+@pytest.mark.parametrize("L,nb,Hkv", [(32, 4, 2), (7, 5, 1), (32, 1, 2), (19, 3, 2), (16, 3, 1), (8, 4, 2),
+                                      (1, 9, 2)])
 def test_transfer_matches_oracle(dtype, F, L, nb, Hkv):
     B, H = 2, 2
     q, k, v, W, alpha, target = make(9700 + F + L + nb + (dtype == torch.bfloat16), B, H, Hkv, nb, L, F, dtype)
@@ -95,3 +96,31 @@ def test_transfer_medium_bf16():
     report("transfer medium bf16", **e)
     assert e["loss"] <= TOL[torch.float32]
     assert e["dW"] <= GRAD_TOL[torch.bfloat16] and e["dalpha"] <= GRAD_TOL[torch.bfloat16]
+
+
+def test_transfer_bench_size_bf16():
+    """The launch bench.py --transfer times: 16 requests x 16 heads x 2048
+    tokens (64 blocks of 32), d = F = 128, bf16.  The layer output of a
+    sampled request from that launch against the oracle, element by element;
+    that request's loss and gradients (a one-request launch) against the
+    oracle; and the full-batch gradients against the ordered sum of the 16
+    one-request launches (the gradient is a sum over requests)."""
+    B, H, L, nb, F = 16, 16, 32, 64, 128
+    q, k, v, W, alpha, target = make(9800, B, H, H, nb, L, F, torch.bfloat16)
+    out = torch.empty((B, H, nb * L, 128), device=DEV)
+    full = hba.transfer(q, k, v, W, alpha, target, L, out=out)
+    b = 11
+    one = [hba.transfer(q[i:i + 1], k[i:i + 1], v[i:i + 1], W, alpha, target[i:i + 1], L) for i in range(B)]
+    ref = oracle.transfer(q[b:b + 1], k[b:b + 1], v[b:b + 1], W, alpha, target[b:b + 1], L)
+    e = errors(one[b], ref)
+    e["out"] = row_rel(out[b:b + 1], ref[0])
+    report("transfer bench size bf16 (request 11)", **e)
+    assert e["loss"] <= TOL[torch.float32] and e["out"] <= TOL[torch.float32]
+    assert e["dW"] <= GRAD_TOL[torch.bfloat16] and e["dalpha"] <= GRAD_TOL[torch.bfloat16]
+    # a sum over requests: the full launch equals the sum of the one-request launches
+    sl = sum(float(o[0][0]) for o in one)
+    sdW = sum(host64(o[1]) for o in one)
+    sda = sum(host64(o[2]) for o in one)
+    assert abs(float(full[0][0]) - sl) <= 1e-6 * sl
+    assert np.linalg.norm(host64(full[1]) - sdW) <= 1e-6 * np.linalg.norm(sdW)
+    assert np.linalg.norm(host64(full[2]) - sda) <= 1e-6 * np.linalg.norm(sda)
