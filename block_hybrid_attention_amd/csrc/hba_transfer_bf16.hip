@@ -80,15 +80,15 @@ __device__ __forceinline__ void split_state_pair(const floatx4 &s0, const floatx
 }
 
 // One 16-byte chunk (8 bf16) of a 32-row tile per thread: row tid/16,
-// columns 8 (tid % 16) ..; rows >= nrows read as zero.  Branch-free (the
-// row is clamped, then the value zeroed), so no control flow makes loads
-// already in flight drain.
+// columns 8 (tid % 16) ..  Rows >= nrows repeat row nrows - 1 (the row is
+// clamped, no branch); they are zeroed where the chunk is staged, one block
+// later.  Zeroing here would place the selects, and with them the wait for
+// the load, right after the load, and the next block's loads would no
+// longer overlap the current block.
 __device__ __forceinline__ uint4 load_chunk(const uint16_t *__restrict__ rows, int nrows, int tid) {
     const int row = tid >> 4, c0 = (tid & 15) * 8;
     const int rr = row < nrows ? row : nrows - 1;
-    const uint4 t = *reinterpret_cast<const uint4 *>(rows + (rr * kXferD + c0));
-    const bool ok = row < nrows;
-    return make_uint4(ok ? t.x : 0u, ok ? t.y : 0u, ok ? t.z : 0u, ok ? t.w : 0u);
+    return *reinterpret_cast<const uint4 *>(rows + (rr * kXferD + c0));
 }
 
 // The same chunk of v for the transposed tile vT[column][token]: row tid % 32,
@@ -97,9 +97,14 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t *__restrict__ rows, i
 __device__ __forceinline__ uint4 load_chunk_t(const uint16_t *__restrict__ rows, int nrows, int tid) {
     const int row = tid & 31, c0 = (tid >> 5) * 8;
     const int rr = row < nrows ? row : nrows - 1;
-    const uint4 t = *reinterpret_cast<const uint4 *>(rows + (rr * kXferD + c0));
-    const bool ok = row < nrows;
-    return make_uint4(ok ? t.x : 0u, ok ? t.y : 0u, ok ? t.z : 0u, ok ? t.w : 0u);
+    return *reinterpret_cast<const uint4 *>(rows + (rr * kXferD + c0));
+}
+
+__device__ __forceinline__ uint4 zero_unless(const uint4 &v, bool ok) {
+    return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
+__device__ __forceinline__ float4 zero_unless(const float4 &v, bool ok) {
+    return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // 1. Forward sweep, bf16 inputs.  Per block, after the staging barrier, each
@@ -184,10 +189,12 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_bf16_kernel(
         asm volatile("" : "+v"(tidv));
         const int li = tidv & 15, lg = (tidv >> 4) & 3, srow = tidv >> 4, scol = (tidv & 15) * 8;
         const int lofs = 4 * lg * D + c0 + li;
-        *reinterpret_cast<uint4 *>(xq + srow * XLD + scol) = cq;
-        *reinterpret_cast<uint4 *>(xk + srow * XLD + scol) = ck;
+        const bool rok = srow < L, tok = (tidv & 31) < L;   // rows of the chunks inside the block
+        *reinterpret_cast<uint4 *>(xq + srow * XLD + scol) = zero_unless(cq, rok);
+        *reinterpret_cast<uint4 *>(xk + srow * XLD + scol) = zero_unless(ck, rok);
         {
-            const uint32_t vw[4] = {cv.x, cv.y, cv.z, cv.w};
+            const uint4 cvz = zero_unless(cv, tok);
+            const uint32_t vw[4] = {cvz.x, cvz.y, cvz.z, cvz.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 vT[((tidv >> 5) * 8 + e) * TLD + (tidv & 31)] = (uint16_t)(vw[e >> 1] >> (16 * (e & 1)));
@@ -461,20 +468,17 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_bf16_kernel(
     }
 }
 
-// Eight fp32 values of a 32-row tile per thread, rows >= nrows zero.
-// Row layout: row tid/16, columns 8 (tid % 16) ..; column layout (for a
-// transposed tile): row tid % 32, columns 8 (tid / 32) ..
+// Eight fp32 values of a 32-row tile per thread (rows >= nrows repeat row
+// nrows - 1, zeroed where staged, as for load_chunk).  Row layout: row
+// tid/16, columns 8 (tid % 16) ..; column layout (for a transposed tile):
+// row tid % 32, columns 8 (tid / 32) ..
 template <bool COLS>
 __device__ __forceinline__ void load_chunk_f32(const float *__restrict__ rows, int nrows, int tid, float4 &lo4,
                                                float4 &hi4) {
     const int row = COLS ? (tid & 31) : (tid >> 4), c0 = COLS ? (tid >> 5) * 8 : (tid & 15) * 8;
     const int rr = row < nrows ? row : nrows - 1;
-    const float4 a = *reinterpret_cast<const float4 *>(rows + (rr * kXferD + c0));
-    const float4 b = *reinterpret_cast<const float4 *>(rows + (rr * kXferD + c0 + 4));
-    const bool ok = row < nrows;
-    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-    lo4 = ok ? a : z;
-    hi4 = ok ? b : z;
+    lo4 = *reinterpret_cast<const float4 *>(rows + (rr * kXferD + c0));
+    hi4 = *reinterpret_cast<const float4 *>(rows + (rr * kXferD + c0 + 4));
 }
 
 // Position of column c (a multiple of 4) of a row stored in the permuted
@@ -602,22 +606,26 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_sweep_bf16_kernel(Tr
         const int srow = tidv >> 4, scol = (tidv & 15) * 8;     // row-layout chunk
         const int trow = tidv & 31, tcol = (tidv >> 5) * 8;     // column-layout chunk
 
-        // A. stage
-        *reinterpret_cast<uint4 *>(xs + srow * XLD + scol) = cx;
-        *reinterpret_cast<uint4 *>(ys + srow * XLD + scol) = cy;
+        // A. stage (rows past the block become zero here)
+        const bool rok = srow < L, tok = trow < L;
+        *reinterpret_cast<uint4 *>(xs + srow * XLD + scol) = zero_unless(cx, rok);
+        *reinterpret_cast<uint4 *>(ys + srow * XLD + scol) = zero_unless(cy, rok);
         {
-            const uint32_t w4[4] = {cxt.x, cxt.y, cxt.z, cxt.w};
+            const uint4 cxz = zero_unless(cxt, tok);
+            const uint32_t w4[4] = {cxz.x, cxz.y, cxz.z, cxz.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) xT[(tcol + e) * TLD + trow] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
         }
         if constexpr (!KEYS) {
-            const uint32_t w4[4] = {cv.x, cv.y, cv.z, cv.w};
+            const uint4 cvz = zero_unless(cv, tok);
+            const uint32_t w4[4] = {cvz.x, cvz.y, cvz.z, cvz.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) uh[(tcol + e) * TLD + trow] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
             if (tidv < kRows) dd[tidv] = cdd;
         } else {
             // dnum^T split into high parts and residuals, dden as row d
-            const float d8[8] = {cd0.x, cd0.y, cd0.z, cd0.w, cd1.x, cd1.y, cd1.z, cd1.w};
+            const float4 c0z = zero_unless(cd0, tok), c1z = zero_unless(cd1, tok);
+            const float d8[8] = {c0z.x, c0z.y, c0z.z, c0z.w, c1z.x, c1z.y, c1z.z, c1z.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const __bf16 hi = (__bf16)d8[e];
@@ -633,8 +641,8 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_sweep_bf16_kernel(Tr
             }
         }
         // the contraction operand waits in registers until phase C
-        const uint4 cvc = cv;
-        const float4 cdc0 = cd0, cdc1 = cd1;
+        const uint4 cvc = zero_unless(cv, rok);
+        const float4 cdc0 = zero_unless(cd0, rok), cdc1 = zero_unless(cd1, rok);
         if (it_ + 1 < a.nb) request(it_ + 1);
         __syncthreads();
 
