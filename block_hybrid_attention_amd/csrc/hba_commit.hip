@@ -296,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     w[j] = __builtin_amdgcn_perm(wb[2 * j + 1][c >> 1], wb[2 * j][c >> 1], sel);
-                *reinterpret_cast<uint4 *>(ws + (8 * bf + c) * P::WLD + 8 * bi) = make_uint4(w[0], w[1], w[2], w[3]);
+                *reinterpret_cast<uint4 *>(ws + wt_off<D>(8 * bf + c, bi)) = make_uint4(w[0], w[1], w[2], w[3]);
             }
         }
         if (do_v) {

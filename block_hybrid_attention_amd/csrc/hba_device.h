@@ -223,6 +223,17 @@ __device__ __forceinline__ void load_w(const T *__restrict__ W, WChunks<T, D, F>
     }
 }
 
+// bf16 W^T tiles [F][D + 8] in LDS are swizzled: the 16-byte chunk q
+// (elements 8q .. 8q+7) of row f sits at chunk q ^ ((f / 16) mod (D / 8)).
+// The transposing writes of store_w put rows 8 apart side by side, and
+// without the swizzle a wave's 16-byte writes shared 8 bank groups; with it
+// they spread over 16, while the MFMA operand reads (16 consecutive rows,
+// one chunk) stay conflict-free.  Element offset of chunk q of row f:
+template <int D>
+__device__ __forceinline__ int wt_off(int f, int q) {
+    return f * (D + 8) + 8 * (q ^ ((f >> 4) & (D / 8 - 1)));
+}
+
 __device__ __forceinline__ uint32_t u4_word(const uint4 &v, int j) {
     return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
 }
@@ -247,7 +258,7 @@ __device__ __forceinline__ void store_w(const WChunks<T, D, F> &wc, T *__restric
                     for (int j = 0; j < 4; ++j)
                         w[j] = __builtin_amdgcn_perm(u4_word(wc.v[8 * it + 2 * j + 1], c >> 1),
                                                      u4_word(wc.v[8 * it + 2 * j], c >> 1), sel);
-                    *reinterpret_cast<uint4 *>(ws + (8 * bf + c) * G::WLD + 8 * bi) =
+                    *reinterpret_cast<uint4 *>(ws + wt_off<D>(8 * bf + c, bi)) =
                         make_uint4(w[0], w[1], w[2], w[3]);
                 }
             }
@@ -282,7 +293,7 @@ __device__ __forceinline__ void project_tile(const T *__restrict__ xs, const T *
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8 *>(xs + (16 * mt + li) * G::XLD + 32 * ks + 8 * lg);
-                const bf16x8 b = *reinterpret_cast<const bf16x8 *>(ws + (16 * nt + li) * G::WLD + 32 * ks + 8 * lg);
+                const bf16x8 b = *reinterpret_cast<const bf16x8 *>(ws + wt_off<D>(16 * nt + li, 4 * ks + lg));
                 acc = mfma_bf16(a, b, acc);
             }
         } else {
@@ -317,7 +328,7 @@ __device__ __forceinline__ void project_rows16(const T *__restrict__ xs, const T
             const bf16x8 a = *reinterpret_cast<const bf16x8 *>(xs + (row0 + li) * G::XLD + 32 * ks + 8 * lg);
 #pragma unroll
             for (int nt = 0; nt < F / 16; ++nt) {
-                const bf16x8 b = *reinterpret_cast<const bf16x8 *>(ws + (16 * nt + li) * G::WLD + 32 * ks + 8 * lg);
+                const bf16x8 b = *reinterpret_cast<const bf16x8 *>(ws + wt_off<D>(16 * nt + li, 4 * ks + lg));
                 u[nt] = mfma_bf16(a, b, u[nt]);
             }
         }
@@ -347,7 +358,7 @@ __device__ __forceinline__ void project_rows16_part(const T *__restrict__ xs, co
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
                 const bf16x8 b =
-                    *reinterpret_cast<const bf16x8 *>(ws + (16 * (nt0 + j) + li) * G::WLD + 32 * ks + 8 * lg);
+                    *reinterpret_cast<const bf16x8 *>(ws + wt_off<D>(16 * (nt0 + j) + li, 4 * ks + lg));
                 u[j] = mfma_bf16(a, b, u[j]);
             }
         }

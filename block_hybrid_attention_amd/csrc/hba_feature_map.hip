@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads, 2) void feature_map_kernel_bf16(FeatureMa
         for (int s_ = 0; s_ < KS; ++s_)
 #pragma unroll
             for (int m = 0; m < NT; ++m) {
-                const bf16x8 aw = *reinterpret_cast<const bf16x8 *>(ws + (16 * m + li) * P::WLD + 32 * s_ + 8 * lg);
+                const bf16x8 aw = *reinterpret_cast<const bf16x8 *>(ws + wt_off<D>(16 * m + li, 4 * s_ + lg));
                 acc[m] = mfma_bf16(aw, xo[t & 1][s_], acc[m]);
             }
         // this wave's half: softmax over the F features of sgn * u

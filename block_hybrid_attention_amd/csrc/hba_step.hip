@@ -484,7 +484,7 @@ __global__ __launch_bounds__(kThreads, 3) void step_kernel_bf16(StepArgs a) {
             const bf16x8 bq = *reinterpret_cast<const bf16x8 *>(qs + (16 * wave + li) * P::XLD + 32 * ks_ + 8 * lg);
 #pragma unroll
             for (int m = 0; m < NT; ++m) {
-                const bf16x8 aw = *reinterpret_cast<const bf16x8 *>(ws + (16 * m + li) * P::WLD + 32 * ks_ + 8 * lg);
+                const bf16x8 aw = *reinterpret_cast<const bf16x8 *>(ws + wt_off<D>(16 * m + li, 4 * ks_ + lg));
                 acc[m] = mfma_bf16(aw, bq, acc[m]);
             }
         }

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kFusedThreads, 2) void step_commit_kernel_bf16(Step
             const bf16x8 bq = *reinterpret_cast<const bf16x8 *>(qs + (16 * grp + li) * P::XLD + 32 * ks_ + 8 * lg);
 #pragma unroll
             for (int m = 0; m < NT; ++m) {
-                const bf16x8 aw = *reinterpret_cast<const bf16x8 *>(ws + (16 * m + li) * P::WLD + 32 * ks_ + 8 * lg);
+                const bf16x8 aw = *reinterpret_cast<const bf16x8 *>(ws + wt_off<D>(16 * m + li, 4 * ks_ + lg));
                 acc[m] = mfma_bf16(aw, bq, acc[m]);
             }
         }
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(kFusedThreads, 2) void step_commit_kernel_bf16(Step
             const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(ks + (16 * grp + li) * P::XLD + 32 * ks_ + 8 * lg);
 #pragma unroll
             for (int m = 0; m < NT; ++m) {
-                const bf16x8 bw = *reinterpret_cast<const bf16x8 *>(ws + (16 * m + li) * P::WLD + 32 * ks_ + 8 * lg);
+                const bf16x8 bw = *reinterpret_cast<const bf16x8 *>(ws + wt_off<D>(16 * m + li, 4 * ks_ + lg));
                 acc[m] = mfma_bf16(ak, bw, acc[m]);
             }
         }

@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_bf16_kernel(
                 const bf16x8 b = lds_bf16x8(xq + t * XLD + 32 * ks + 8 * lg);
 #pragma unroll
                 for (int ft = 0; ft < NFT; ++ft)
-                    x[ft] = mfma_bf16(lds_bf16x8(wt + (16 * ft + li) * WLD + 32 * ks + 8 * lg), b, x[ft]);
+                    x[ft] = mfma_bf16(lds_bf16x8(wt + wt_off<D>(16 * ft + li, 4 * ks + lg)), b, x[ft]);
                 fence();
             }
             float mx = -INFINITY;
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_bf16_kernel(
                 const bf16x8 xa = lds_bf16x8(xk + (16 * tt + li) * XLD + 32 * ks + 8 * lg);
 #pragma unroll
                 for (int ft = 0; ft < NFT; ++ft)
-                    x[ft] = mfma_bf16(xa, lds_bf16x8(wt + (16 * ft + li) * WLD + 32 * ks + 8 * lg), x[ft]);
+                    x[ft] = mfma_bf16(xa, lds_bf16x8(wt + wt_off<D>(16 * ft + li, 4 * ks + lg)), x[ft]);
                 fence();
             }
             float inv[4];
@@ -659,7 +659,7 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_sweep_bf16_kernel(Tr
                 const bf16x8 b = lds_bf16x8(xs + t * XLD + 32 * ks + 8 * lg);
 #pragma unroll
                 for (int ft = 0; ft < NFT; ++ft)
-                    x[ft] = mfma_bf16(lds_bf16x8(wt + (16 * ft + li) * WLD + 32 * ks + 8 * lg), b, x[ft]);
+                    x[ft] = mfma_bf16(lds_bf16x8(wt + wt_off<D>(16 * ft + li, 4 * ks + lg)), b, x[ft]);
                 fence();
             }
             float mx = -INFINITY;
@@ -701,7 +701,7 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_sweep_bf16_kernel(Tr
                 const bf16x8 xa = lds_bf16x8(ys + (16 * tt + li) * XLD + 32 * ks + 8 * lg);
 #pragma unroll
                 for (int ft = 0; ft < NFT; ++ft)
-                    x[ft] = mfma_bf16(xa, lds_bf16x8(wt + (16 * ft + li) * WLD + 32 * ks + 8 * lg), x[ft]);
+                    x[ft] = mfma_bf16(xa, lds_bf16x8(wt + wt_off<D>(16 * ft + li, 4 * ks + lg)), x[ft]);
                 fence();
             }
             float inv[4];
