@@ -225,10 +225,11 @@ __device__ __forceinline__ void load_w(const T *__restrict__ W, WChunks<T, D, F>
 
 // bf16 W^T tiles [F][D + 8] in LDS are swizzled: the 16-byte chunk q
 // (elements 8q .. 8q+7) of row f sits at chunk q ^ ((f / 16) mod (D / 8)).
-// The transposing writes of store_w put rows 8 apart side by side, and
-// without the swizzle a wave's 16-byte writes shared 8 bank groups; with it
-// they spread over 16, while the MFMA operand reads (16 consecutive rows,
-// one chunk) stay conflict-free.  Element offset of chunk q of row f:
+// One instruction of the transposing writes of store_w covers rows 8 apart,
+// which the 17-chunk row stride alone maps to the same few bank groups; the
+// swizzle spreads them (the step kernel's LDS bank-conflict cycles halved).
+// The MFMA operand reads (16 consecutive rows, one chunk each) keep their
+// pattern.  Element offset of chunk q of row f:
 template <int D>
 __device__ __forceinline__ int wt_off(int f, int q) {
     return f * (D + 8) + 8 * (q ^ ((f >> 4) & (D / 8 - 1)));

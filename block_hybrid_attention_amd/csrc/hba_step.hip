@@ -373,7 +373,7 @@ template <int D, int F>
 struct StepGeomBf16 {
     using P = ProjGeom<uint16_t, D, F>;
     static constexpr int KA = kRows + 2 * F;   // K of the merged contraction
-    static constexpr int KP = KA + 8;          // A row stride in bf16 (conflict-free reads)
+    static constexpr int KP = KA + 8;          // A row stride in bf16 (16-byte aligned rows)
     static constexpr int q_off = 0;
     static constexpr int k_off = P::x_bytes;
     static constexpr int w_off = 2 * P::x_bytes;
@@ -670,7 +670,6 @@ __global__ __launch_bounds__(kThreads, 3) void step_kernel_bf16(StepArgs a) {
     }
 }
 
-// compute units of the current device (cached per device; 0 if unknown)
 template <typename T, int D, int F>
 static hipError_t launch_step_t(const StepArgs &a, hipStream_t stream) {
     if constexpr (sizeof(T) == 2) {

@@ -36,8 +36,9 @@ struct XbGeom {
     static constexpr int D = kXferD, P2 = 2 * F, NFT = F / 16, NPT = P2 / 16;
     static constexpr int XLD = ProjGeom<uint16_t, kXferD, F>::XLD;   // bf16 row tiles [32][XLD]
     static constexpr int WLD = ProjGeom<uint16_t, kXferD, F>::WLD;   // W^T [F][WLD]
-    // bf16 tiles with the token index contiguous, [column][TLD]: 80-byte rows
-    // put the 16 lanes of a 16-byte read on 16 disjoint groups of 4 banks
+    // bf16 tiles with the token index contiguous, [column][TLD]: 80-byte
+    // rows (16-byte aligned operand reads).  The 96-byte stride that avoids
+    // LDS bank conflicts on these reads measured no faster.
     static constexpr int TLD = kRows + 8;
     static constexpr int PQLD = P2 + 8;   // phi(q) rows [32][PQLD], permuted per 32 features
     // byte offsets
@@ -93,7 +94,7 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t *__restrict__ rows, i
 
 // The same chunk of v for the transposed tile vT[column][token]: row tid % 32,
 // columns 8 (tid / 32) ..  Each wave then covers all 32 rows of two column
-// chunks, so its 2-byte writes into vT land on 32 different banks.
+// chunks (its 2-byte writes into vT measured free of bank conflicts).
 __device__ __forceinline__ uint4 load_chunk_t(const uint16_t *__restrict__ rows, int nrows, int tid) {
     const int row = tid & 31, c0 = (tid >> 5) * 8;
     const int rr = row < nrows ? row : nrows - 1;
@@ -123,7 +124,7 @@ template <int F>
 __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_bf16_kernel(TransferArgs a) {
     using G = XbGeom<F>;
     constexpr int D = kXferD, P2 = G::P2, NFT = G::NFT, NPT = G::NPT;
-    constexpr int XLD = G::XLD, WLD = G::WLD, TLD = G::TLD, PQLD = G::PQLD;
+    constexpr int XLD = G::XLD, TLD = G::TLD, PQLD = G::PQLD;
     __shared__ __attribute__((aligned(16))) unsigned char smem[G::total];
     uint16_t *xq = reinterpret_cast<uint16_t *>(smem + G::xq), *xk = reinterpret_cast<uint16_t *>(smem + G::xk),
              *vT = reinterpret_cast<uint16_t *>(smem + G::vT), *wt = reinterpret_cast<uint16_t *>(smem + G::wt),
@@ -531,7 +532,7 @@ template <int F, bool KEYS>
 __global__ __launch_bounds__(kXferThreads, 1) void transfer_sweep_bf16_kernel(TransferArgs a) {
     using G = XsGeom<F, KEYS>;
     constexpr int D = kXferD, P2 = G::P2, NFT = F / 16, FW = G::FW, NA = D / 16 + 1;
-    constexpr int XLD = G::XLD, WLD = G::WLD, TLD = G::TLD, CLD = G::CLD, PXLD = G::PXLD;
+    constexpr int XLD = G::XLD, TLD = G::TLD, CLD = G::CLD, PXLD = G::PXLD;
     constexpr int NWT = F == 128 ? 8 : 4;   // dW tiles per wave
     __shared__ __attribute__((aligned(16))) unsigned char smem[G::total];
     uint16_t *wt = reinterpret_cast<uint16_t *>(smem + G::wt), *xs = reinterpret_cast<uint16_t *>(smem + G::xs),
