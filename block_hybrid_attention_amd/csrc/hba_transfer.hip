@@ -72,41 +72,33 @@ int64_t transfer_workspace_floats(int64_t BH, int64_t N, int F) { return xfer_ws
 
 // Eight consecutive elements of one of the 32 rows of a token tile
 // (512 threads: row = tid / 16, columns 8 (tid % 16) ..), zero past nrows.
-template <typename T>
-__device__ __forceinline__ void load8(const T *__restrict__ rows, int nrows, int tid, float (&x)[8]) {
+__device__ __forceinline__ void load8(const float *__restrict__ rows, int nrows, int tid, float (&x)[8]) {
     const int row = tid >> 4, c0 = (tid & 15) * 8;
     if (row < nrows) {
-        const T *p = rows + (int64_t)row * kXferD + c0;
-        if constexpr (sizeof(T) == 2) {
-            const uint4 w = *reinterpret_cast<const uint4 *>(p);
-            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = bf16_bits_to_f32((ws[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-        } else {
-            const float4 a = *reinterpret_cast<const float4 *>(p);
-            const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-            x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-        }
+        const float *p = rows + (int64_t)row * kXferD + c0;
+        const float4 a = *reinterpret_cast<const float4 *>(p);
+        const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
     } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = 0.f;
     }
 }
 
-template <typename T, int XLD>
-__device__ __forceinline__ void stage_rows_f32(const T *__restrict__ rows, int nrows, float *dst, int tid) {
+template <int XLD>
+__device__ __forceinline__ void stage_rows_f32(const float *__restrict__ rows, int nrows, float *dst, int tid) {
     float x[8];
-    load8<T>(rows, nrows, tid, x);
+    load8(rows, nrows, tid, x);
     float *p = dst + (tid >> 4) * XLD + (tid & 15) * 8;
     *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
     *reinterpret_cast<float4 *>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
 }
 
-template <typename T, int TLD>
-__device__ __forceinline__ void stage_cols_f32(const T *__restrict__ rows, int nrows, float *dstT, int tid) {
+template <int TLD>
+__device__ __forceinline__ void stage_cols_f32(const float *__restrict__ rows, int nrows, float *dstT, int tid) {
     float x[8];
-    load8<T>(rows, nrows, tid, x);
+    load8(rows, nrows, tid, x);
     const int row = tid >> 4, c0 = (tid & 15) * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dstT[(c0 + e) * TLD + row] = x[e];
@@ -133,7 +125,7 @@ __device__ __forceinline__ void stage_colsT_f32(const float *__restrict__ rows, 
 }
 
 // 1. Forward sweep.
-template <typename T, int F>
+template <int F>
 __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_kernel(TransferArgs a) {
     using G = XferGeom<F>;
     constexpr int D = kXferD, P2 = 2 * F, NFT = P2 / 16, TLD = G::TLD;
@@ -148,9 +140,9 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_kernel(Trans
     const int h = (int)(bh % a.H);
     const int L = a.L;
     const int64_t N = (int64_t)a.nb * L;
-    const T *qg = static_cast<const T *>(a.q) + bh * N * D;
-    const T *kg = static_cast<const T *>(a.k) + (bh / a.G) * N * D;
-    const T *vg = static_cast<const T *>(a.v) + (bh / a.G) * N * D;
+    const float *qg = static_cast<const float *>(a.q) + bh * N * D;
+    const float *kg = static_cast<const float *>(a.k) + (bh / a.G) * N * D;
+    const float *vg = static_cast<const float *>(a.v) + (bh / a.G) * N * D;
     const float *tg = a.target + bh * N * D;
     const float w = 1.f / (1.f + __expf(-a.alpha[h]));
     const float log2w = __log2f(w);
@@ -169,9 +161,9 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_kernel(Trans
 #pragma unroll 1
     for (int n = 0; n < a.nb; ++n) {
         const int64_t t0 = (int64_t)n * L;
-        stage_rows_f32<T, G::XLD>(qg + t0 * D, L, xq, tid);
-        stage_rows_f32<T, G::XLD>(kg + t0 * D, L, xk, tid);
-        stage_cols_f32<T, TLD>(vg + t0 * D, L, vT, tid);
+        stage_rows_f32<G::XLD>(qg + t0 * D, L, xq, tid);
+        stage_rows_f32<G::XLD>(kg + t0 * D, L, xk, tid);
+        stage_cols_f32<TLD>(vg + t0 * D, L, vT, tid);
         stage_colsT_f32<P2, TLD>(pqg + t0 * P2, L, phqT, tid);
         stage_colsT_f32<P2, TLD>(pkg + t0 * P2, L, phkT, tid);
         // this lane's teacher outputs (rows 16 rt + 4 lg + r, column c0 + li),
@@ -341,7 +333,7 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_kernel(Trans
 //   dphi(k) = V G^T + Gz, then G^T += dnum^T phi(Q), Gz += sum dden phi(q).
 // The state X^T [d][2F] lives in registers split by feature: wave w holds
 // features fb .. fb + 2F/8 - 1 (fb = w 2F/8) for all d value columns.
-template <typename T, int F, bool KEYS>
+template <int F, bool KEYS>
 __global__ __launch_bounds__(kXferThreads, 1) void transfer_sweep_kernel(TransferArgs a) {
     using G = XferGeom<F>;
     constexpr int D = kXferD, P2 = 2 * F, TLD = G::TLD;
@@ -359,9 +351,9 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_sweep_kernel(Transfe
     const int L = a.L;
     const int64_t N = (int64_t)a.nb * L;
     const int64_t npad = (N + 3) & ~int64_t(3);
-    const T *qg = static_cast<const T *>(a.q) + bh * N * D;
-    const T *kg = static_cast<const T *>(a.k) + (bh / a.G) * N * D;
-    const T *vg = static_cast<const T *>(a.v) + (bh / a.G) * N * D;
+    const float *qg = static_cast<const float *>(a.q) + bh * N * D;
+    const float *kg = static_cast<const float *>(a.k) + (bh / a.G) * N * D;
+    const float *vg = static_cast<const float *>(a.v) + (bh / a.G) * N * D;
     const XferWs ws = xfer_ws((int64_t)a.B * a.H, N, F);
     const float *dng = a.ws + ws.dnum + bh * N * D;
     const float *ddg = a.ws + ws.dden + bh * npad;
@@ -387,11 +379,11 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_sweep_kernel(Transfe
         const int64_t t0 = (int64_t)n * L;
         // only the side whose gradient this sweep takes needs its rows
         if (KEYS)
-            stage_rows_f32<T, G::XLD>(kg + t0 * D, L, xk, tid);
+            stage_rows_f32<G::XLD>(kg + t0 * D, L, xk, tid);
         else
-            stage_rows_f32<T, G::XLD>(qg + t0 * D, L, xq, tid);
-        stage_cols_f32<T, TLD>(vg + t0 * D, L, vT, tid);
-        stage_cols_f32<float, TLD>(dng + t0 * D, L, dnT, tid);
+            stage_rows_f32<G::XLD>(qg + t0 * D, L, xq, tid);
+        stage_cols_f32<TLD>(vg + t0 * D, L, vT, tid);
+        stage_cols_f32<TLD>(dng + t0 * D, L, dnT, tid);
         stage_colsT_f32<P2, TLD>(pqg + t0 * P2, L, phqT, tid);
         stage_colsT_f32<P2, TLD>(pkg + t0 * P2, L, phkT, tid);
         if (tid < kRows) dd[tid] = tid < L ? ddg[t0 + tid] : 0.f;
@@ -565,9 +557,9 @@ static hipError_t launch_transfer_t(const TransferArgs &a, hipStream_t stream) {
             e = launch_feature_map(fq, false, (int)D, F, stream, a.B);
             if (e == hipSuccess) e = launch_feature_map(fk, false, (int)D, F, stream, a.B);
             const dim3 grid((unsigned)pairs), block(kXferThreads);
-            if (e == hipSuccess) e = launch_kernel(transfer_forward_kernel<T, F>, grid, block, a, stream);
-            if (e == hipSuccess) e = launch_kernel(transfer_sweep_kernel<T, F, false>, grid, block, a, stream);
-            if (e == hipSuccess) e = launch_kernel(transfer_sweep_kernel<T, F, true>, grid, block, a, stream);
+            if (e == hipSuccess) e = launch_kernel(transfer_forward_kernel<F>, grid, block, a, stream);
+            if (e == hipSuccess) e = launch_kernel(transfer_sweep_kernel<F, false>, grid, block, a, stream);
+            if (e == hipSuccess) e = launch_kernel(transfer_sweep_kernel<F, true>, grid, block, a, stream);
         }
     }
     if (e != hipSuccess) return e;
