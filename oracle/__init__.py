@@ -20,7 +20,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hba_oracle.c")
-_LIB = os.path.join(_HERE, "libhba_oracle.so")
+# HBA_ORACLE_LIB points the loader at another build of hba_oracle.c (the
+# pin-sensitivity test loads builds with a planted mistake this way)
+_LIB = os.environ.get("HBA_ORACLE_LIB") or os.path.join(_HERE, "libhba_oracle.so")
 
 _f64p = ctypes.POINTER(ctypes.c_double)
 _i32p = ctypes.POINTER(ctypes.c_int32)

@@ -45,9 +45,19 @@
 #include <omp.h>
 #endif
 
+/* Planted mistakes for the pin-sensitivity test (tests/test_oracle_mutants.py):
+ * built with -DORC_MUTANT=n, the oracle makes mistake n (each a plausible
+ * slip: a dropped term, a wrong sign, index or operand) so that the test can
+ * check that some pin fails.  The default build, ORC_MUTANT = 0, is the
+ * oracle as specified; every ORC_M(n) below is then a constant 0. */
+#ifndef ORC_MUTANT
+#define ORC_MUTANT 0
+#endif
+#define ORC_M(n) (ORC_MUTANT == (n))
+
 /* Key/value row block of query head h of request b. */
 static int64_t kv_index(int b, int h, int H, int Hkv) {
-    return (int64_t)b * Hkv + h / (H / Hkv);
+    return (int64_t)b * Hkv + (ORC_M(10) ? h % Hkv : h / (H / Hkv));
 }
 
 /* Largest |score| for which exp() of the unshifted score stays far from fp64
@@ -64,7 +74,7 @@ static void phi_row(int d, int F, const double *x, const double *W,
                     double *u, double *phi) {
     for (int f = 0; f < F; ++f) {
         double acc = 0.0;
-        for (int i = 0; i < d; ++i) acc += x[i] * W[(int64_t)i * F + f];
+        for (int i = 0; i < d; ++i) acc += x[i] * W[ORC_M(3) ? (int64_t)f * d + i : (int64_t)i * F + f];
         u[f] = acc;
     }
     double mx = u[0], mn = u[0];
@@ -79,7 +89,7 @@ static void phi_row(int d, int F, const double *x, const double *W,
     }
     for (int f = 0; f < F; ++f) {
         phi[f] = exp(u[f] - mx) / sp;
-        phi[F + f] = exp(-u[f] + mn) / sn;
+        phi[F + f] = ORC_M(1) ? exp(u[f] - mx) / sp : exp(-u[f] + mn) / (ORC_M(2) ? sp : sn);
     }
 }
 
@@ -140,8 +150,8 @@ int orc_commit(int B, int H, int Hkv, int T, int d, int F, const int32_t *n_vali
             const double *vt = v + (kvh * T + t) * (int64_t)d;
             phi_row(d, F, kt, Wh, u, p);
             for (int f = 0; f < P2; ++f) {
-                Z[f] += p[f];
-                for (int n = 0; n < d; ++n) S[(int64_t)f * d + n] += p[f] * vt[n];
+                if (!ORC_M(4)) Z[f] += p[f];
+                for (int n = 0; n < d; ++n) S[(int64_t)f * d + n] += p[f] * (ORC_M(5) ? kt[n] : vt[n]);
             }
         }
         free(u);
@@ -189,9 +199,10 @@ int orc_step(int B, int H, int Hkv, int L, int d, int F, const double *q,
             double sm_den = 0.0;
             for (int n = 0; n < d; ++n) num[n] = 0.0;
             for (int j = 0; j < L; ++j) {
+                if (ORC_M(9) && j == i) continue;
                 double sc = 0.0;
                 for (int n = 0; n < d; ++n) sc += qi[n] * kb[(int64_t)j * d + n];
-                sc *= scale;
+                sc *= ORC_M(6) ? 1.0 : scale;
                 if (!(fabs(sc) <= ORC_MAX_ABS_SCORE)) bad |= 4;
                 double a = exp(sc);
                 sm_den += a;
@@ -207,7 +218,7 @@ int orc_step(int B, int H, int Hkv, int L, int d, int F, const double *q,
                 num[n] += lin;
             }
             /* shared normaliser */
-            double den = w * sm_den + lin_den;
+            double den = (ORC_M(7) ? 1.0 : w) * sm_den + (ORC_M(8) ? 0.0 : lin_den);
             for (int n = 0; n < d; ++n) ob[(int64_t)i * d + n] = num[n] / den;
         }
         free(u);
@@ -247,12 +258,12 @@ int orc_prefix_softmax(int B, int H, int Hkv, int L, int d, int max_prefix,
             const double *qi = qb + (int64_t)i * d;
             double den = 0.0;
             for (int n = 0; n < d; ++n) num[n] = 0.0;
-            for (int j = 0; j < P + L; ++j) {
+            for (int j = 0; j < P + (ORC_M(11) ? 0 : L); ++j) {
                 const double *kj = j < P ? Kb + (int64_t)j * d : kb + (int64_t)(j - P) * d;
                 const double *vj = j < P ? Vb + (int64_t)j * d : vb + (int64_t)(j - P) * d;
                 double sc = 0.0;
                 for (int n = 0; n < d; ++n) sc += qi[n] * kj[n];
-                sc *= scale;
+                sc *= ORC_M(12) ? 1.0 : scale;
                 if (!(fabs(sc) <= ORC_MAX_ABS_SCORE)) bad |= 4;
                 double a = exp(sc);
                 den += a;
@@ -299,7 +310,7 @@ static void phi_backward(int F, const double *phi, const double *dphi, double *d
         sn += phi[F + f] * dphi[F + f];
     }
     for (int f = 0; f < F; ++f)
-        du[f] = phi[f] * (dphi[f] - sp) - phi[F + f] * (dphi[F + f] - sn);
+        du[f] = phi[f] * (dphi[f] - sp) + (ORC_M(17) ? 1.0 : -1.0) * phi[F + f] * (dphi[F + f] - sn);
 }
 
 int orc_transfer(int B, int H, int Hkv, int n_blocks, int L, int d, int F,
@@ -340,6 +351,13 @@ int orc_transfer(int B, int H, int Hkv, int n_blocks, int L, int d, int F,
         double *gW = pW + bh * d * F;
         for (int n = 0; n < n_blocks; ++n) {
             const int64_t i0 = (int64_t)n * L;
+            for (int64_t t = i0; ORC_M(18) && t < i0 + L; ++t) {
+                phi_row(d, F, kb + t * d, Wh, u, p);
+                for (int f = 0; f < P2; ++f) {
+                    Z[f] += p[f];
+                    for (int c = 0; c < d; ++c) S[(int64_t)f * d + c] += p[f] * vb[t * d + c];
+                }
+            }
             for (int64_t i = i0; i < i0 + L; ++i) {
                 const double *qi = qb + i * d;
                 /* within-block softmax branch */
@@ -373,14 +391,14 @@ int orc_transfer(int B, int H, int Hkv, int n_blocks, int L, int d, int F,
                     pl[bh] += e * e;
                     go += 2.0 * e * o[c];
                 }
-                dden[i] = -go / den;
+                dden[i] = ORC_M(13) ? go / den : -go / den;
                 for (int c = 0; c < d; ++c) dnum[i * d + c] = 2.0 * (o[c] - tb[i * d + c]) / den;
                 double gw = dden[i] * smd;
                 for (int c = 0; c < d; ++c) gw += dnum[i * d + c] * smn[c];
                 pw[bh] += gw;
                 /* through phi(q_i) into W */
                 for (int f = 0; f < P2; ++f) {
-                    double acc = Z[f] * dden[i];
+                    double acc = ORC_M(14) ? 0.0 : Z[f] * dden[i];
                     for (int c = 0; c < d; ++c) acc += S[(int64_t)f * d + c] * dnum[i * d + c];
                     dp[f] = acc;
                 }
@@ -389,7 +407,7 @@ int orc_transfer(int B, int H, int Hkv, int n_blocks, int L, int d, int F,
                     for (int f = 0; f < F; ++f) gW[(int64_t)r * F + f] += qi[r] * du[f];
             }
             /* commit block n */
-            for (int64_t t = i0; t < i0 + L; ++t) {
+            for (int64_t t = i0; !ORC_M(18) && t < i0 + L; ++t) {
                 phi_row(d, F, kb + t * d, Wh, u, p);
                 for (int f = 0; f < P2; ++f) {
                     Z[f] += p[f];
@@ -407,7 +425,7 @@ int orc_transfer(int B, int H, int Hkv, int n_blocks, int L, int d, int F,
                 const double *kt = kb + t * d, *vt = vb + t * d;
                 phi_row(d, F, kt, Wh, u, p);
                 for (int f = 0; f < P2; ++f) {
-                    double acc = Gz[f];
+                    double acc = ORC_M(16) ? 0.0 : Gz[f];
                     for (int c = 0; c < d; ++c) acc += G[(int64_t)f * d + c] * vt[c];
                     dp[f] = acc;
                 }
@@ -423,7 +441,7 @@ int orc_transfer(int B, int H, int Hkv, int n_blocks, int L, int d, int F,
                 }
             }
         }
-        pw[bh] *= w * (1.0 - w);
+        pw[bh] *= ORC_M(15) ? w : w * (1.0 - w);
         free(S); free(Z); free(phq); free(dnum); free(dden);
         free(u); free(p); free(dp); free(du); free(smn); free(o);
     }
