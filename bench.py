@@ -223,6 +223,55 @@ def transfer_bench(args, torch, hba, wl, dev):
                       "frac_of_bf16_mfma_peak": issued / (ms * 1e-3) / 1e12 / 2500.0}), flush=True)
 
 
+def batch_sweep(args, torch, hba, wl, dev):
+    """hba_step (bf16, H=16, d=F=128, L=32) over batch sizes, with enough
+    rotating state sets (> 600 MB) that the 256 MB Infinity Cache holds none
+    of them.  A least-squares line t = t0 + items / R over the batches that
+    fill the CUs at least once splits the launch time into a fixed part t0
+    (ramp-up, and the last workgroups' epilogue and output drain) and the
+    marginal HBM rate R of the state stream."""
+    H, L, d, F = 16, 32, 128, 128
+    batches = [int(x) for x in (args.batch if args.batch != "128" else "16,32,48,64,96,112,128,144,160,192").split(",")]
+    rows = []
+    for B in batches:
+        g = wl.generator(31 + B, dev)
+        W = wl.feature_weights(H, d, F, torch.bfloat16, g, dev)
+        q, k, v = wl.block_qkv(B, H, L, d, torch.bfloat16, g, dev)
+        per_set = B * H * (2 * F * d + 2 * F) * 4
+        nsets = max(2, -(-600_000_000 // per_set))
+        sets = [(wl.normal((B, H, 2 * F, d), 0.01, torch.float32, g, dev),
+                 torch.rand((B, H, 2 * F), generator=g, device=dev) * 20 + 1) for _ in range(nsets)]
+        out = torch.empty((B, H, L, d), device=dev)
+        it = [0]
+
+        def fn():
+            S, Z = sets[it[0] % nsets]
+            it[0] += 1
+            hba.step(q, k, v, W, S, Z, out=out)
+
+        ms = _time_launches(torch, fn, max(args.warmup, nsets), args.steps, torch.cuda.current_stream())
+        nb = step_bytes(B, H, L, d, F)
+        rows.append({"batch": B, "items": B * H, "us": ms * 1e3, "TBps": nb / (ms * 1e-3) / 1e12,
+                     "state_sets": nsets})
+        print(json.dumps({"mode": "batch_sweep", **rows[-1]}), flush=True)
+        del sets
+        torch.cuda.empty_cache()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    # three step workgroups are resident per CU; below that the launch is one partial round
+    fit = [r for r in rows if r["items"] >= 3 * cus]
+    if len(fit) >= 2:
+        n = len(fit)
+        mx = sum(r["items"] for r in fit) / n
+        my = sum(r["us"] for r in fit) / n
+        slope = sum((r["items"] - mx) * (r["us"] - my) for r in fit) / sum((r["items"] - mx) ** 2 for r in fit)
+        t0 = my - slope * mx
+        item_bytes = (step_bytes(128, H, L, d, F) - H * d * F * 2) / (128 * H)
+        print(json.dumps({"mode": "batch_sweep_fit", "batches": [r["batch"] for r in fit],
+                          "fixed_us": t0, "us_per_item": slope,
+                          "marginal_TBps": item_bytes / (slope * 1e-6) / 1e12,
+                          "marginal_frac_of_8TBps": item_bytes / (slope * 1e-6) / 8e12}), flush=True)
+
+
 def decode_loop(args, torch, hba, wl, dev):
     """One hybrid layer through a block-diffusion decode: per 32-token block,
     8 denoising steps (hba_step) then hba_commit of the block; 32 requests."""
@@ -345,6 +394,8 @@ def main():
     ap.add_argument("--blocks", type=int, default=256)
     ap.add_argument("--transfer", action="store_true",
                     help="time stage-1 attention transfer (loss, dW, dalpha) at 16 x 16 heads x 2048 tokens")
+    ap.add_argument("--batch-sweep", action="store_true",
+                    help="time hba_step over batch sizes (--batch, default 16..192) and fit fixed + marginal cost")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel (torch.neg) "
                          "10 times, to calibrate HBM byte counters")
@@ -378,6 +429,8 @@ def main():
         return decode_loop(args, torch, hba, wl, dev)
     if args.transfer:
         return transfer_bench(args, torch, hba, wl, dev)
+    if args.batch_sweep:
+        return batch_sweep(args, torch, hba, wl, dev)
     c = wl.serving_b128()
     B, H, L, d, F = c.batch, c.heads, c.block, c.head_dim, c.feat
     plen = torch.tensor(c.prefix, dtype=torch.int32)
