@@ -320,8 +320,8 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
     // the old state goes straight into the accumulators: row
     // f_base + 16 mt + 4 lg + r of this half, columns 32 q + 2 li (+ 1) of
     // N-tiles 2q (2q + 1).
-    // Multi-chunk commits load it at entry; a one-block commit loads it once
-    // phi is in LDS, so the accumulators are not live during the prologue.
+    // Multi-chunk commits load it at entry; a one-block commit right after
+    // its staging barrier.
     floatx4 acc[MT][NE];
     auto load_state = [&]() {
 #pragma unroll
@@ -346,6 +346,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
         const int nrows = nv - t0 < kRows ? nv - t0 : kRows;
         stage(t0, nrows, !kResidentW || t0 == 0);
         __syncthreads();
+        // one-block commit: the state is requested once the staging loads have
+        // landed, so it does not queue ahead of them, and its latency overlaps
+        // the projection and phi
+        if constexpr (!kResidentW) load_state();
         // waves 0-1: u = k W for tokens 16w .. 16w+15 (log2 domain), and the
         // max (or min) and sum of this half's softmax per token
         floatx4 u[NT];
@@ -378,7 +382,6 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
                 for (int nt = 0; nt < NT; ++nt) row[16 * nt + li] = fast_exp2(u[nt][r] - mref[r]) * inv[r];
             }
         }
-        if constexpr (!kResidentW) load_state();
         __syncthreads();
         if (zf >= 0 && zf < F) {
             float zs = 0.f;
