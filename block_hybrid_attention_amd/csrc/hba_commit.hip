@@ -238,8 +238,21 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int half = (int)blockIdx.x & 1;     // 0: softmax(kW) rows, 1: softmax(-kW) rows
-    const int bh = (int)blockIdx.x >> 1;
+    // half 0: softmax(kW) rows, 1: softmax(-kW) rows.  Workgroups are dealt
+    // to the 8 XCDs in turn, so in each full group of 16 the two halves of a
+    // (request, head) sit 8 apart, on the same XCD: the second reads k and v
+    // from that XCD's L2.  A last partial group pairs neighbours.
+    int half, bh;
+    {
+        const int g = (int)blockIdx.x, grp = g >> 4;
+        if ((grp + 1) * 8 <= a.B * a.H) {
+            half = (g >> 3) & 1;
+            bh = grp * 8 + (g & 7);
+        } else {
+            half = g & 1;
+            bh = g >> 1;
+        }
+    }
     const int b = bh / a.H, h = bh - b * a.H;
     const int T_ = a.T;
     int nv = a.n_valid ? a.n_valid[b] : T_;
