@@ -7,27 +7,26 @@
 //
 // One workgroup (4 waves) per (request, head).  The step is bound by HBM
 // bandwidth: the fp32 state S (2F x d, 128 KB at F = d = 128) is read once and
-// dominates the bytes.  Design:
-//   * Every wave owns d/4 output columns and streams its column slice of S
-//     through a ring of registers: the first kRing 4-row steps are requested
-//     at kernel entry, and each step consumed in the main loop requests the
-//     step kRing ahead, so ~16 KB per wave stay in flight from the first
-//     instruction to the last.
-//   * q, k and W are staged in LDS (W transposed in registers on the way).
-//     The prologue is spread evenly over the four waves: wave w takes query
-//     rows 16(w/2) .. +15 and feature half w%2 of u = q W, plus the block
-//     scores of those rows (bf16 MFMA for bf16 inputs: exact products, fp32
-//     accumulation; fp32 MFMA for fp32 inputs).  phi(q), phi(q).Z and the
-//     softmax weights are formed in the accumulator layout, where a query row
-//     sits in one 16-lane DPP row, so every reduction is four DPP steps; the
-//     two waves sharing a row swap partial maxima and sums through LDS.
-//     Exponentials run in the base-2 domain.
-//   * Per query the exponent shift c_i = max(m_i + ln w, ln lin_den_i) is
-//     applied to both branches, so w exp(s - c) <= 1 and e^{-c} lin_den <= 1.
-//   * Both numerators become ONE contraction
+// dominates the bytes.  Both kernels below:
+//   * give every wave d/4 output columns and stream its column slice of S
+//     through registers, with part of the stream requested at kernel entry,
+//     so the state's latency overlaps the staging and the prologue;
+//   * stage q, k and W in LDS (W transposed in registers on the way), then
+//     form phi(q), phi(q).Z and the block softmax weights in the MFMA
+//     accumulator layout, with exponentials in the base-2 domain;
+//   * apply one exponent shift per query, c_i = max(m_i + ln w, ln lin_den_i),
+//     to both branches, so w exp(s - c) <= 1 and e^{-c} lin_den <= 1;
+//   * run both numerators as ONE contraction
 //       [w e^{s_i - c_i} | e^{-c_i} phi(q_i)]  x  [V ; S]     (K = L + 2F)
-//     on fp32 MFMA; its A operand reuses the LDS of the staged q, k and W.
-//     The shared denominator is applied at the store.
+//     whose A operand reuses the LDS of the staged q, k and W, and apply the
+//     shared denominator at the store.
+// step_kernel_f32 (fp32 inputs) streams S in 4-row K-steps, 24 in flight,
+// spreads the prologue over all four waves (two per query row, swapping
+// partial maxima and sums through LDS) and contracts on fp32 MFMA.
+// step_kernel_bf16 (bf16 inputs, the serving path) streams S in 32-row
+// chunks, two to four in flight; waves 0-1 form phi(q) and waves 2-3 the
+// block scores; the contraction runs on bf16 MFMA with split operands (see
+// the note above that kernel).
 #include "hba_device.h"
 #include "hba_internal.h"
 
