@@ -268,6 +268,30 @@ def test_step_commit_shapes_slots_gate(dtype, d, F, L):
         assert e <= TOL[dtype]
 
 
+@pytest.mark.parametrize("T", [32, 45])
+def test_commit_grid_with_partial_group(T):
+    """bf16 commit over 20 (request, head) pairs: the two state halves of each
+    pair go to workgroups 8 apart in whole groups of 16 and to neighbours in
+    the last, partial group (pairs 16..19); every state against the oracle,
+    through a slot map that reverses the requests."""
+    g = gen(7400 + T)
+    B, H, d, F = 5, 4, 128, 128
+    dt = torch.bfloat16
+    W = wl.feature_weights(H, d, F, dt, g, DEV)
+    pk, pv = wl.normal((B, H, T, d), 1, dt, g, DEV), wl.normal((B, H, T, d), 1, dt, g, DEV)
+    slot = torch.arange(B - 1, -1, -1, dtype=torch.int32, device=DEV)
+    S, Z = zeros_pool(B, H, F, d)
+    S += 0.01 * torch.randn(S.shape, generator=g, device=DEV)
+    Z += torch.rand(Z.shape, generator=g, device=DEV)
+    S0, Z0 = S.clone(), Z.clone()
+    hba.commit(pk, pv, W, S, Z, slot=slot)
+    Sr, Zr = oracle.commit(S0, Z0, pk, pv, W, slot=slot)
+    errs = dict(S=state_rel(S, Sr), Z=state_rel(Z[..., None], Zr[..., None]))
+    report(f"commit B={B} H={H} T={T}", **errs)
+    for e in errs.values():
+        assert e <= TOL[dt]
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("L", [1, 32])
 def test_empty_state_is_block_softmax_and_matches_comparator(dtype, L):
