@@ -1,7 +1,10 @@
 // hba_api.cpp -- the C ABI declared in include/hba.h: host-side validation
 // and dispatch to the gfx950 kernels.  Nothing here allocates device memory
-// or synchronises; every call enqueues at most one kernel on the caller's
-// stream.
+// or synchronises; every call only enqueues kernels on the caller's stream:
+// one for the step, the commit, the fused step + commit on its bf16 d = 128
+// path and the unsplit comparator; two for the split comparator (the split
+// kernel and the merge) and for the fused call's other shapes (step, then
+// commit); up to six for the stage-1 transfer.
 #include "hba.h"
 
 #include <hip/hip_runtime.h>

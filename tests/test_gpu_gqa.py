@@ -12,7 +12,7 @@ import torch
 import block_hybrid_attention_amd as hba
 import oracle
 from block_hybrid_attention_amd import workloads as wl
-from parity import TOL, report, row_rel, state_rel
+from parity import check, report, row_rel, state_rel
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -65,8 +65,7 @@ def test_gqa_step_and_commit_match_oracle(dtype, d, F, Hkv):
     ref = oracle.step(q, k, v, W, Sr, Zr, gate=gate, slot=slot)
     errs = dict(out=row_rel(out, ref), S=state_rel(S, Sr), Z=state_rel(Z[..., None], Zr[..., None]))
     report(f"gqa step+commit {dtype} d={d} F={F} H={H} Hkv={Hkv}", **errs)
-    for e in errs.values():
-        assert e <= TOL[dtype]
+    check(errs, dtype)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -90,8 +89,7 @@ def test_gqa_step_commit_matches_oracle(dtype, d, F, L):
     Sr, Zr = oracle.commit(Sp, Zp, k, v, W, n_valid=n_valid)
     errs = dict(out=row_rel(out, ref), S=state_rel(S, Sr), Z=state_rel(Z[..., None], Zr[..., None]))
     report(f"gqa step_commit {dtype} d={d} F={F} L={L}", **errs)
-    for e in errs.values():
-        assert e <= TOL[dtype]
+    check(errs, dtype)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -107,7 +105,7 @@ def test_gqa_comparator_matches_oracle(dtype, d):
     ref = oracle.prefix_softmax(q, k, v, Kc, Vc, prefix_len=plen)
     err = row_rel(out, ref)
     report(f"gqa comparator {dtype} d={d}", out=err)
-    assert err <= TOL[dtype]
+    check(dict(out=err), dtype)
 
 
 def test_gqa_serving_shape_equals_repeated_heads_bitwise():
@@ -150,4 +148,4 @@ def test_gqa_serving_shape_equals_repeated_heads_bitwise():
     ref = oracle.step(q[idx], k[idx], v[idx], W, Sr, Zr, gate=gate)
     err = row_rel(o1[idx], ref)
     report("gqa serving-shape step sample", out=err)
-    assert err <= TOL[dtype]
+    check(dict(out=err), dtype)

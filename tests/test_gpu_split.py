@@ -8,7 +8,7 @@ import torch
 import block_hybrid_attention_amd as hba
 import oracle
 from block_hybrid_attention_amd import workloads as wl
-from parity import TOL, report, row_rel
+from parity import check, report, row_rel
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -37,7 +37,7 @@ def test_split_comparator_matches_oracle(dtype, d, n_split):
     ref = oracle.prefix_softmax(q, k, v, Kc, Vc, prefix_len=plen)
     err = row_rel(out, ref)
     report(f"split comparator {dtype} d={d} n_split={n_split}", out=err)
-    assert err <= TOL[dtype]
+    check(dict(out=err), dtype)
 
 
 @pytest.mark.parametrize("L", [1, 7])
@@ -51,7 +51,7 @@ def test_split_comparator_short_blocks(L):
     ref = oracle.prefix_softmax(q, k, v, Kc, Vc)
     err = row_rel(out, ref)
     report(f"split comparator L={L}", out=err)
-    assert err <= TOL[dtype]
+    check(dict(out=err), dtype)
 
 
 def test_split_comparator_small_batch_long_prefix():
@@ -71,7 +71,7 @@ def test_split_comparator_small_batch_long_prefix():
     ref = oracle.prefix_softmax(q[idx], k[idx], v[idx], Kc[idx], Vc[idx])
     err = row_rel(out[idx], ref)
     report(f"split comparator B=8 P=8192 auto n_split={ns}", vs_unsplit=agree, out=err)
-    assert agree <= TOL[dtype] and err <= TOL[dtype]
+    check(dict(vs_unsplit=agree, out=err), dtype)
 
 
 def test_split_workspace_reuse_and_size_check():

@@ -10,7 +10,7 @@ import torch
 import block_hybrid_attention_amd as hba
 import oracle
 from block_hybrid_attention_amd import workloads as wl
-from parity import TOL, report, row_rel, state_rel
+from parity import check, report, row_rel, state_rel
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -58,8 +58,7 @@ def test_step_commit_matches_oracle(dtype, d, F, L):
     assert torch.equal(S[0], S1[0]) and torch.equal(Z[0], Z1[0])   # n_valid 0: untouched by the fused call
     errs = dict(out=row_rel(out, ref), S=state_rel(S, Sr), Z=state_rel(Z[..., None], Zr[..., None]))
     report(f"step_commit {dtype} d={d} F={F} L={L}", **errs)
-    for e in errs.values():
-        assert e <= TOL[dtype]
+    check(errs, dtype)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -78,8 +77,7 @@ def test_step_commit_agrees_with_separate_calls(dtype):
     hba.commit(k, v, W, S2, Z2)
     errs = dict(out=row_rel(out_f, out_s), S=state_rel(S, S2), Z=state_rel(Z[..., None], Z2[..., None]))
     report(f"step_commit vs step + commit {dtype}", **errs)
-    for e in errs.values():
-        assert e <= TOL[dtype]
+    check(errs, dtype)
 
 
 def test_step_commit_medium_bf16():
@@ -101,5 +99,4 @@ def test_step_commit_medium_bf16():
     Sr, Zr = oracle.commit(Sp, Zp, k, v, W)
     errs = dict(out=row_rel(out, ref), S=state_rel(S, Sr), Z=state_rel(Z[..., None], Zr[..., None]))
     report("step_commit medium bf16", **errs)
-    for e in errs.values():
-        assert e <= TOL[dtype]
+    check(errs, dtype)
