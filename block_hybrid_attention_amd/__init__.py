@@ -23,12 +23,14 @@ from .pool import StatePool  # noqa: F401  (re-exported)
 
 __all__ = ["feature_map", "step", "commit", "prefix_softmax", "StatePool", "HbaError",
            "library_path", "load_library", "abi_version", "step_commit", "prefix_softmax_workspace_bytes",
-           "prefix_softmax_auto_split", "transfer", "transfer_workspace_bytes"]
+           "prefix_softmax_auto_split", "transfer", "transfer_workspace_bytes", "prefix_softmax_noalloc",
+           "NOALLOC_SCRATCH_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libhba.so")
 
 HBA_F32, HBA_BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024   # HBA_NOALLOC_SCRATCH_BYTES in include/hba.h
 _DTYPE = {torch.float32: HBA_F32, torch.bfloat16: HBA_BF16}
 _STATUS = {0: "HBA_OK", 1: "HBA_ERR_NULL", 2: "HBA_ERR_SHAPE", 3: "HBA_ERR_UNSUPPORTED",
            4: "HBA_ERR_DTYPE", 5: "HBA_ERR_ALIGN", 6: "HBA_ERR_CAPACITY", 7: "HBA_ERR_HIP"}
@@ -71,6 +73,7 @@ def load_library():
         lib.hba_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         i32, i64 = ctypes.c_int32, ctypes.c_int64
         lib.hba_prefix_softmax_split.argtypes = [sp, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp]
+        lib.hba_prefix_softmax_split_noalloc.argtypes = [sp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.hba_prefix_softmax_auto_split.argtypes = [sp, i32]
         lib.hba_prefix_softmax_auto_split.restype = i32
         lib.hba_prefix_softmax_workspace_bytes.argtypes = [sp, i32]
@@ -296,6 +299,32 @@ def prefix_softmax(q, k, v, Kc, Vc, prefix_len=None, out=None, stream=None, n_sp
     _call(lib.hba_prefix_softmax_split, "hba_prefix_softmax_split", ctypes.byref(shape), P, n_split,
           _p(prefix_len), _p(q), _p(k), _p(v), kc, vc, _p(workspace), workspace.numel() * 4, _p(out),
           _stream(stream))
+    return out
+
+
+def prefix_softmax_noalloc(q, k, v, Kc, Vc, out, n_split=None, prefix_len=None, stream=None):
+    """The split comparator through hba_prefix_softmax_split_noalloc: the
+    partials go to the library's fixed per-device scratch array, so the call
+    allocates nothing (``out`` is the caller's).  n_split None takes the
+    library's choice.  Calls that overlap on one device race."""
+    lib = load_library()
+    B, H, L, d = q.shape
+    P = Kc.shape[2]
+    dt = _in_dtype(q, k, v, Kc, Vc)
+    Hkv = _kv_heads(H, k)
+    for t, nm in ((k, "k"), (v, "v")):
+        _check(t, (B, Hkv, L, d), q.dtype, nm)
+    _check(Kc, (B, Hkv, P, d), q.dtype, "Kc")
+    _check(Vc, (B, Hkv, P, d), q.dtype, "Vc")
+    _check(prefix_len, (B,), torch.int32, "prefix_len")
+    _check(out, (B, H, L, d), torch.float32, "out")
+    _dev(q, k, v, Kc, Vc, prefix_len, out)
+    shape = Shape(B, H, L, d, 64, dt, 0, Hkv)
+    if n_split is None:
+        n_split = int(lib.hba_prefix_softmax_auto_split(ctypes.byref(shape), P))
+    _call(lib.hba_prefix_softmax_split_noalloc, "hba_prefix_softmax_split_noalloc", ctypes.byref(shape), P,
+          n_split, _p(prefix_len), _p(q), _p(k), _p(v), _p(Kc) if P > 0 else None, _p(Vc) if P > 0 else None,
+          _p(out), _stream(stream))
     return out
 
 

@@ -75,7 +75,7 @@ const char *hba_status_string(hba_status st) {
     return "unknown status";
 }
 
-int32_t hba_abi_version(void) { return 5; }
+int32_t hba_abi_version(void) { return 6; }
 
 hba_status hba_feature_map(const hba_shape *shape, int64_t n_rows, const void *x, const void *W,
                            float *phi, void *stream) {
@@ -174,10 +174,12 @@ int64_t hba_prefix_softmax_workspace_bytes(const hba_shape *shape, int32_t n_spl
     return 4 * (int64_t)shape->batch * shape->heads * n_split * shape->block * (shape->head_dim + 2);
 }
 
-hba_status hba_prefix_softmax_split(const hba_shape *shape, int32_t max_prefix, int32_t n_split,
-                                    const int32_t *prefix_len, const void *q, const void *k, const void *v,
-                                    const void *Kc, const void *Vc, float *workspace, int64_t workspace_bytes,
-                                    float *out, void *stream) {
+namespace {
+
+// Host checks of the comparator's arguments apart from the workspace.
+hba_status check_prefix(const hba_shape *shape, int32_t max_prefix, int32_t n_split, const int32_t *prefix_len,
+                        const void *q, const void *k, const void *v, const void *Kc, const void *Vc,
+                        const float *out) {
     hba_status st = check_common(shape, true, false);
     if (st != HBA_OK) return st;
     const int G = kv_group(shape);
@@ -187,16 +189,45 @@ hba_status hba_prefix_softmax_split(const hba_shape *shape, int32_t max_prefix, 
     if (shape->batch == 0) return HBA_OK;
     if (!q || !k || !v || !out) return HBA_ERR_NULL;
     if (max_prefix > 0 && (!Kc || !Vc)) return HBA_ERR_NULL;
-    if (n_split > 1 && !workspace) return HBA_ERR_NULL;
-    if (n_split > 1 && workspace_bytes < hba_prefix_softmax_workspace_bytes(shape, n_split)) return HBA_ERR_CAPACITY;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
-        (max_prefix > 0 && (!aligned16(Kc) || !aligned16(Vc))) || (prefix_len && !aligned4(prefix_len)) ||
-        (n_split > 1 && !aligned16(workspace)))
+        (max_prefix > 0 && (!aligned16(Kc) || !aligned16(Vc))) || (prefix_len && !aligned4(prefix_len)))
         return HBA_ERR_ALIGN;
-    hba::PrefixArgs a{prefix_len, q, k, v, Kc, Vc, out, shape->batch, shape->heads, shape->block, max_prefix, G,
-                      n_split > 1 ? workspace : nullptr, n_split};
+    return HBA_OK;
+}
+
+hba_status launch_prefix(const hba_shape *shape, int32_t max_prefix, int32_t n_split, const int32_t *prefix_len,
+                         const void *q, const void *k, const void *v, const void *Kc, const void *Vc,
+                         float *workspace, float *out, void *stream) {
+    hba::PrefixArgs a{prefix_len, q, k, v, Kc, Vc, out, shape->batch, shape->heads, shape->block, max_prefix,
+                      kv_group(shape), n_split > 1 ? workspace : nullptr, n_split};
     return from_hip(hba::launch_prefix_softmax(a, shape->in_dtype == HBA_BF16, shape->head_dim,
                                                static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+hba_status hba_prefix_softmax_split(const hba_shape *shape, int32_t max_prefix, int32_t n_split,
+                                    const int32_t *prefix_len, const void *q, const void *k, const void *v,
+                                    const void *Kc, const void *Vc, float *workspace, int64_t workspace_bytes,
+                                    float *out, void *stream) {
+    hba_status st = check_prefix(shape, max_prefix, n_split, prefix_len, q, k, v, Kc, Vc, out);
+    if (st != HBA_OK || shape->batch == 0) return st;
+    if (n_split > 1 && !workspace) return HBA_ERR_NULL;
+    if (n_split > 1 && workspace_bytes < hba_prefix_softmax_workspace_bytes(shape, n_split)) return HBA_ERR_CAPACITY;
+    if (n_split > 1 && !aligned16(workspace)) return HBA_ERR_ALIGN;
+    return launch_prefix(shape, max_prefix, n_split, prefix_len, q, k, v, Kc, Vc, workspace, out, stream);
+}
+
+hba_status hba_prefix_softmax_split_noalloc(const hba_shape *shape, int32_t max_prefix, int32_t n_split,
+                                            const int32_t *prefix_len, const void *q, const void *k,
+                                            const void *v, const void *Kc, const void *Vc, float *out,
+                                            void *stream) {
+    hba_status st = check_prefix(shape, max_prefix, n_split, prefix_len, q, k, v, Kc, Vc, out);
+    if (st != HBA_OK || shape->batch == 0) return st;
+    if (hba_prefix_softmax_workspace_bytes(shape, n_split) > hba::kStaticScratchBytes) return HBA_ERR_CAPACITY;
+    float *ws = nullptr;
+    if (n_split > 1 && hba::static_scratch(&ws) != hipSuccess) return HBA_ERR_HIP;
+    return launch_prefix(shape, max_prefix, n_split, prefix_len, q, k, v, Kc, Vc, ws, out, stream);
 }
 
 int64_t hba_transfer_workspace_bytes(const hba_shape *shape, int32_t n_blocks) {

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "hba.h"
+
 namespace hba {
 
 // Row r of head h in batch b (b < gridDim.z) reads x at
@@ -99,6 +101,12 @@ hipError_t launch_transfer(const TransferArgs &a, bool dtype_bf16, int F, hipStr
 
 // Largest key split of the comparator.
 constexpr int kMaxPrefixSplit = 64;
+
+// The comparator's library-held scratch (hba_prefix_softmax_split_noalloc):
+// its size, and the address of the current device's copy.
+constexpr int64_t kStaticScratchBytes = HBA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+hipError_t static_scratch(float **ptr);
 
 // Compute units of the current device (0 if the runtime cannot say).
 int device_cus();

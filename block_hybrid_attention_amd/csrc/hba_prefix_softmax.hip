@@ -22,6 +22,9 @@
 // contiguous run of key tiles and write a normalised partial output with its
 // running max and sum; prefix_combine_kernel then merges the NS partials of
 // each query with the usual rescaling (the same algebra that merges waves).
+#include <atomic>
+#include <mutex>
+
 #include "hba_device.h"
 #include "hba_internal.h"
 
@@ -564,6 +567,37 @@ static hipError_t launch_prefix_t(const PrefixArgs &a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const unsigned slices = (unsigned)((a.L * D / 4 + kThreads - 1) / kThreads);
     return launch_kernel(prefix_combine_kernel<D>, dim3(pairs, slices), dim3(kThreads), a, stream);
+}
+
+// Partials of hba_prefix_softmax_split_noalloc: a fixed array in device
+// memory, one copy per device, held until the process ends.  Host code never
+// passes `scratch` itself to a kernel (on the host it names a stand-in, not a
+// device address); it asks static_scratch() for the device's address, taken
+// once per device with hipGetSymbolAddress.
+static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
+
+hipError_t static_scratch(float **ptr) {
+    static std::atomic<float *> addr[kMaxDevices];
+    static std::mutex init;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    float *p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(init);
+        p = addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            void *sym = nullptr;
+            e = hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!sym) return hipErrorInvalidSymbol;
+            p = static_cast<float *>(sym);
+            addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 hipError_t launch_prefix_softmax(const PrefixArgs &a, bool bf16, int d, hipStream_t stream) {

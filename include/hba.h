@@ -14,7 +14,9 @@
  * Conventions shared by every call
  *   - Pure C.  Every buffer is caller-owned device memory (pointers from
  *     hipMalloc or a framework allocator); the library allocates nothing and
- *     keeps no global state, so calls are thread-safe.
+ *     keeps no global state, so calls are thread-safe.  The one exception is
+ *     hba_prefix_softmax_split_noalloc, which uses a fixed scratch array the
+ *     library holds per device (see there).
  *   - Calls enqueue kernels on `stream` (a hipStream_t passed as void*; NULL
  *     is the default stream) and return without synchronising.  A fault on
  *     the device surfaces at the caller's next synchronisation.
@@ -217,6 +219,35 @@ int32_t hba_prefix_softmax_auto_split(const hba_shape *shape, int32_t max_prefix
  * 4 B H n_split L (d + 2) otherwise, -1 for an invalid shape or n_split. */
 int64_t hba_prefix_softmax_workspace_bytes(const hba_shape *shape, int32_t n_split);
 
+/* Bytes of the library-held scratch behind hba_prefix_softmax_split_noalloc
+ * (16 MiB per device). */
+#define HBA_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+
+/* hba_prefix_softmax_split without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The split partials go to a
+ * fixed array of HBA_NOALLOC_SCRATCH_BYTES in device memory that the library
+ * holds, one copy per device, until the process ends; its address is looked
+ * up once per device, on the first call made with that device current.  A
+ * call uses the array of the device current when it is made, which must be
+ * the device of `stream` and of the buffers.  The call allocates nothing.  Same kernels and the same results as
+ * hba_prefix_softmax_split with a caller workspace.
+ *   Every call on one device shares that device's array, and the array keeps
+ *   the last call's partials: calls that overlap on one device (concurrent
+ *   streams, or host threads) race and give undefined results.  Calls
+ *   ordered on one stream are safe.  Nothing in the array needs to start at
+ *   zero.
+ * Arguments: as hba_prefix_softmax_split, without workspace and
+ * workspace_bytes.
+ * Errors: as hba_prefix_softmax_split; HBA_ERR_CAPACITY when
+ * hba_prefix_softmax_workspace_bytes(shape, n_split) exceeds
+ * HBA_NOALLOC_SCRATCH_BYTES (nothing is launched); HBA_ERR_HIP when the
+ * array's address cannot be obtained. */
+hba_status hba_prefix_softmax_split_noalloc(const hba_shape *shape, int32_t max_prefix, int32_t n_split,
+                                            const int32_t *prefix_len, const void *q, const void *k,
+                                            const void *v, const void *Kc, const void *Vc, float *out,
+                                            void *stream);
+
 /* Stage-1 attention transfer (section 3.2): for the hybrid layer of section
  * 3.1 run over whole training sequences of N = n_blocks * block tokens per
  * (request, head) -- the queries of block n see exact softmax over block n
@@ -264,8 +295,9 @@ int64_t hba_transfer_workspace_bytes(const hba_shape *shape, int32_t n_blocks);
 /* Static description of a status code (never NULL). */
 const char *hba_status_string(hba_status status);
 
-/* Library ABI version, currently 5 (2 added hba_step_commit, 3 added
- * hba_shape.kv_heads, 4 added the split comparator, 5 hba_transfer). */
+/* Library ABI version, currently 6 (2 added hba_step_commit, 3 added
+ * hba_shape.kv_heads, 4 added the split comparator, 5 hba_transfer,
+ * 6 hba_prefix_softmax_split_noalloc). */
 int32_t hba_abi_version(void);
 
 #ifdef __cplusplus

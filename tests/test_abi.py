@@ -38,12 +38,12 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"hba_feature_map", "hba_step", "hba_commit", "hba_prefix_softmax", "hba_step_commit",
             "hba_prefix_softmax_split", "hba_prefix_softmax_auto_split", "hba_prefix_softmax_workspace_bytes",
-            "hba_transfer", "hba_transfer_workspace_bytes",
+            "hba_transfer", "hba_transfer_workspace_bytes", "hba_prefix_softmax_split_noalloc",
             "hba_status_string", "hba_abi_version"} <= set(names)
     L = lib()
     for n in names:
         assert hasattr(L, n), n
-    assert hba.abi_version() == 5
+    assert hba.abi_version() == 6
 
 
 def test_status_strings():
@@ -200,6 +200,32 @@ def test_split_comparator_validation():
     # without a device the choice falls back to one split; bad shapes give 1 too
     assert L.hba_prefix_softmax_auto_split(ctypes.byref(sh), 1 << 15) == 1
     assert L.hba_prefix_softmax_auto_split(None, 128) == 1
+
+
+@no_gpu_only
+def test_noalloc_comparator_validation():
+    """The allocation-free comparator: host checks as the split comparator's,
+    partials beyond the library's scratch array refused with
+    HBA_ERR_CAPACITY before any device call; with no device, a call that
+    passes every host check fails with HBA_ERR_HIP and launches nothing."""
+    L = lib()
+    EHIP = 7
+
+    def call(sh, P=128, ns=4, Kc=A, out=A2, q=A):
+        return L.hba_prefix_softmax_split_noalloc(ctypes.byref(sh), P, ns, None, q, A, A, Kc, A, out, None)
+
+    sh = shape()
+    assert call(sh, ns=0) == ESHAPE
+    assert call(sh, ns=65) == ESHAPE
+    assert call(sh, Kc=None) == ENULL
+    assert call(sh, out=None) == ENULL
+    assert call(sh, q=MIS) == EALIGN
+    assert call(shape(kv_heads=3)) == ESHAPE
+    assert call(shape(batch=0)) == OK
+    big = shape(batch=64, heads=16)
+    assert L.hba_prefix_softmax_workspace_bytes(ctypes.byref(big), 16) > 16 * 1024 * 1024
+    assert call(big, ns=16) == ECAP
+    assert call(sh, ns=4) == EHIP
 
 
 @no_gpu_only
