@@ -471,3 +471,38 @@ def test_zero_batch_noop_on_device():
     out = hba.step(q, q, q, W, S, Z)
     hba.commit(q, q, W, S, Z)
     assert out.shape == (0, 2, 32, 64) and float(S.abs().sum()) == 0.0
+
+
+# ------------------------------------------- one-block commit at serving shapes
+@pytest.mark.parametrize("B,T,F,Hkv", [(128, 32, 128, 16), (37, 7, 128, 16), (64, 17, 64, 4), (40, 32, 128, 2)])
+def test_commit_one_block_serving_shapes(B, T, F, Hkv):
+    """The one-block bf16 commit at serving batch sizes (up to 128 requests x
+    16 heads, two workgroups per pair): blocks shorter than 32, ragged n_valid
+    with zeros, a slot map into a larger pool, grouped key/value heads; every
+    state against the oracle, untouched slots and n_valid = 0 pairs bitwise."""
+    H, d = 16, 128
+    dt = torch.bfloat16
+    g = gen(7700 + B + T + F + Hkv)
+    W = wl.feature_weights(H, d, F, dt, g, DEV)
+    k, v = wl.normal((B, Hkv, T, d), 1, dt, g, DEV), wl.normal((B, Hkv, T, d), 1, dt, g, DEV)
+    slots = B + 5
+    slot = torch.randperm(slots, generator=g, device=DEV)[:B].to(torch.int32)
+    n_valid = torch.randint(0, T + 1, (B,), generator=g, device=DEV, dtype=torch.int32)
+    n_valid[::9] = 0
+    S, Z = zeros_pool(slots, H, F, d)
+    S += 0.05 * torch.randn(S.shape, generator=g, device=DEV)
+    Z += torch.rand(Z.shape, generator=g, device=DEV)
+    S0, Z0 = S.clone(), Z.clone()
+    hba.commit(k, v, W, S, Z, n_valid=n_valid, slot=slot)
+    Sr, Zr = oracle.commit(S0, Z0, k, v, W, n_valid=n_valid, slot=slot)
+    used = set(slot.tolist())
+    for sl in range(slots):
+        if sl not in used:
+            assert torch.equal(S[sl], S0[sl]) and torch.equal(Z[sl], Z0[sl])
+    for b in range(B):
+        if int(n_valid[b]) == 0:
+            sl = int(slot[b])
+            assert torch.equal(S[sl], S0[sl]) and torch.equal(Z[sl], Z0[sl])
+    errs = dict(S=state_rel(S, Sr), Z=state_rel(Z[..., None], Zr[..., None]))
+    report(f"one-block commit B={B} T={T} F={F} Hkv={Hkv}", **errs)
+    check(errs, dt)
