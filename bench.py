@@ -463,10 +463,11 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: K back-to-back steps on the launch stream, with a HIP
-    # event between segments of about K/20 launches (never between every
-    # launch: those packets would sit between the kernels).  The mean launch
-    # duration is total / K; the spread is that of the segment means.
-    nseg = max(1, min(20, args.steps))
+    # event between segments of at least 5 launches (at most 20 segments;
+    # never an event between every launch: those packets would sit between
+    # the kernels and add to every step).  The mean launch duration is
+    # total / K; the spread is that of the segment means.
+    nseg = max(1, min(20, args.steps // 5))
     bounds = [round(i * args.steps / nseg) for i in range(nseg + 1)]
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(nseg + 1)]
     torch.cuda.synchronize()
