@@ -48,20 +48,41 @@ __device__ __forceinline__ void split_pk_bf16(float a, float b, uint32_t &hi, ui
     lo = cvt_pk_bf16(a - ha, b - hb);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+// Exchanges across the 16-lane rows of a wave with the gfx950 permlane
+// swaps (one VALU instruction each, no LDS round trip).  With both operands
+// equal to v, permlane16_swap leaves lane l holding {v[l], v[l ^ 16]} and
+// permlane32_swap {v[l], v[l ^ 32]}, in an order that depends on l.
+__device__ __forceinline__ void pair16(float v, float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
 }
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
-    return v;
+__device__ __forceinline__ void pair32(float v, float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+// Reductions over lanes l, l ^ 16, l ^ 32, l ^ 48 (the same position in the
+// four rows): first the pair l, l ^ 16, then l, l ^ 32.  Each step combines
+// the same two values as a shuffle by 16 then by 32 would (operands only
+// swap places), so the results are bitwise those of the shuffle form.
+__device__ __forceinline__ float xrow_max(float v) {
+    float a, b;
+    pair16(v, a, b);
+    pair32(fmaxf(a, b), a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float xrow_min(float v) {
+    float a, b;
+    pair16(v, a, b);
+    pair32(fminf(a, b), a, b);
+    return fminf(a, b);
+}
+__device__ __forceinline__ float xrow_sum(float v) {
+    float a, b;
+    pair16(v, a, b);
+    pair32(a + b, a, b);
+    return a + b;
 }
 
 // Reductions over the 16 lanes of a DPP row (lanes 16g .. 16g+15): rotate by
@@ -91,6 +112,11 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += dpp_f<kDppQuadSwap2>(v);
     return v + dpp_f<kDppQuadSwap1>(v);
 }
+
+// Whole-wave reductions: within each 16-lane row by DPP, then across rows.
+__device__ __forceinline__ float wave_max(float v) { return xrow_max(row16_max(v)); }
+__device__ __forceinline__ float wave_min(float v) { return xrow_min(row16_min(v)); }
+__device__ __forceinline__ float wave_sum(float v) { return xrow_sum(row16_sum(v)); }
 
 __device__ __forceinline__ floatx4 mfma_f32(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);

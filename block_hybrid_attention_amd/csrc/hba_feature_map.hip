@@ -135,8 +135,7 @@ __global__ __launch_bounds__(kThreads, 2) void feature_map_kernel_bf16(FeatureMa
                 acc[m][r] *= sgn2;
                 mx = fmaxf(mx, acc[m][r]);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        mx = xrow_max(mx);
         float sm = 0.f;
 #pragma unroll
         for (int m = 0; m < NT; ++m)
@@ -145,8 +144,7 @@ __global__ __launch_bounds__(kThreads, 2) void feature_map_kernel_bf16(FeatureMa
                 acc[m][r] = fast_exp2(acc[m][r] - mx);
                 sm += acc[m][r];
             }
-        sm += __shfl_xor(sm, 16, kWave);
-        sm += __shfl_xor(sm, 32, kWave);
+        sm = xrow_sum(sm);
         const float is = 1.0f / sm;
         float *prow = ph + (16 * qgrp + li) * G::PLD + half * F + 4 * lg;
 #pragma unroll

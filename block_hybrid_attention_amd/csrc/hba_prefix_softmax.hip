@@ -250,8 +250,7 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(PrefixArgs a) {
                 x[r] = (j0 + 4 * lg + r) < nkeys ? s[nt][r] * kScaleLog2 : -INFINITY;
                 tmax = fmaxf(tmax, x[r]);
             }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+            tmax = xrow_max(tmax);
             const float mnew = fmaxf(m[nt], tmax);   // finite: every tile has a valid key
             const float corr = __builtin_amdgcn_exp2f(m[nt] - mnew);
             float rs = 0.f;
@@ -260,8 +259,7 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(PrefixArgs a) {
                 p[nt][r] = __builtin_amdgcn_exp2f(x[r] - mnew);
                 rs += p[nt][r];
             }
-            rs += __shfl_xor(rs, 16, kWave);
-            rs += __shfl_xor(rs, 32, kWave);
+            rs = xrow_sum(rs);
             l[nt] = l[nt] * corr + rs;
             m[nt] = mnew;
 #pragma unroll
@@ -434,8 +432,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel_bf16(PrefixArgs a) 
                     x[e] = key < nkeys ? sc[e >> 2][nt][e & 3] * kScaleLog2 : -INFINITY;
                     tmax = fmaxf(tmax, x[e]);
                 }
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+                tmax = xrow_max(tmax);
                 const float mnew = fmaxf(m[nt], tmax);   // finite: every tile has a valid key
                 const float corr = __builtin_amdgcn_exp2f(m[nt] - mnew);
                 float rs = 0.f, pv[8];
@@ -444,8 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel_bf16(PrefixArgs a) 
                     pv[e] = __builtin_amdgcn_exp2f(x[e] - mnew);
                     rs += pv[e];
                 }
-                rs += __shfl_xor(rs, 16, kWave);
-                rs += __shfl_xor(rs, 32, kWave);
+                rs = xrow_sum(rs);
                 l[nt] = l[nt] * corr + rs;
                 m[nt] = mnew;
 #pragma unroll

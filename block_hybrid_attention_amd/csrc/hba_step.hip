@@ -506,10 +506,8 @@ __global__ __launch_bounds__(kThreads, 3) void step_kernel_bf16(StepArgs a) {
                 mn = fminf(mn, acc[m][r]);
             }
         // the query's F features are spread over the four lane groups
-        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        mn = fminf(mn, __shfl_xor(mn, 16, kWave));
-        mn = fminf(mn, __shfl_xor(mn, 32, kWave));
+        mx = xrow_max(mx);
+        mn = xrow_min(mn);
         float sp = 0.f, sn = 0.f;
 #pragma unroll
         for (int m = 0; m < NT; ++m)
@@ -518,10 +516,8 @@ __global__ __launch_bounds__(kThreads, 3) void step_kernel_bf16(StepArgs a) {
                 sp += fast_exp2(acc[m][r] - mx);
                 sn += fast_exp2(mn - acc[m][r]);
             }
-        sp += __shfl_xor(sp, 16, kWave);
-        sp += __shfl_xor(sp, 32, kWave);
-        sn += __shfl_xor(sn, 16, kWave);
-        sn += __shfl_xor(sn, 32, kWave);
+        sp = xrow_sum(sp);
+        sn = xrow_sum(sn);
         const float ip = 1.0f / sp, in_ = 1.0f / sn;
         float zd = 0.f;
         T *ah = Ahi + qi * G::KP + kRows + 4 * lg;
@@ -548,8 +544,7 @@ __global__ __launch_bounds__(kThreads, 3) void step_kernel_bf16(StepArgs a) {
             *reinterpret_cast<uint2 *>(ah + F + 16 * m) = make_uint2(hn[0], hn[1]);
             *reinterpret_cast<uint2 *>(al + F + 16 * m) = make_uint2(ln[0], ln[1]);
         }
-        zd += __shfl_xor(zd, 16, kWave);
-        zd += __shfl_xor(zd, 32, kWave);
+        zd = xrow_sum(zd);
         if (lg == 0) r_ld[qi] = zd;   // lin_den = phi(q).Z
     } else {
         const int row0 = 16 * (wave - 2);

@@ -201,8 +201,7 @@ __global__ __launch_bounds__(kFusedThreads, 2) void step_commit_kernel_bf16(Step
                 acc[m][r] *= sgn2;
                 mx = fmaxf(mx, acc[m][r]);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        mx = xrow_max(mx);
         float sm = 0.f;
 #pragma unroll
         for (int m = 0; m < NT; ++m)
@@ -211,8 +210,7 @@ __global__ __launch_bounds__(kFusedThreads, 2) void step_commit_kernel_bf16(Step
                 acc[m][r] = fast_exp2(acc[m][r] - mx);
                 sm += acc[m][r];
             }
-        sm += __shfl_xor(sm, 16, kWave);
-        sm += __shfl_xor(sm, 32, kWave);
+        sm = xrow_sum(sm);
         const float is = 1.0f / sm;
         float zd = 0.f;
         T *ah = Ahi + qi * G::KP + kRows + half * F + 4 * lg;
@@ -229,8 +227,7 @@ __global__ __launch_bounds__(kFusedThreads, 2) void step_commit_kernel_bf16(Step
             *reinterpret_cast<uint2 *>(ah + 16 * m) = make_uint2(hw[0], hw[1]);
             *reinterpret_cast<uint2 *>(al + 16 * m) = make_uint2(lw[0], lw[1]);
         }
-        zd += __shfl_xor(zd, 16, kWave);
-        zd += __shfl_xor(zd, 32, kWave);
+        zd = xrow_sum(zd);
         if (lg == 0) rowv(qi)[half] = zd;
         if (wave >= 2) {
             // block softmax of the same queries, relative to the row maximum
@@ -292,8 +289,7 @@ __global__ __launch_bounds__(kFusedThreads, 2) void step_commit_kernel_bf16(Step
             *reinterpret_cast<uint2 *>(Khi + f * G::KT + t0) = make_uint2(hw[0], hw[1]);
             *reinterpret_cast<uint2 *>(Klo + f * G::KT + t0) = make_uint2(lw[0], lw[1]);
             float zt = (e0 + e1) + (e2 + e3);   // this lane's four tokens
-            zt += __shfl_xor(zt, 16, kWave);
-            zt += __shfl_xor(zt, 32, kWave);
+            zt = xrow_sum(zt);
             if (lg == 0) zk[grp * 2 * F + f] = zt;
         }
     }

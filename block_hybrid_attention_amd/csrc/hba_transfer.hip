@@ -428,8 +428,7 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_sweep_kernel(Transfe
             for (int j = 0; j < FT; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc += phx[(fb + 16 * j + 4 * lg + r) * TLD + 16 * it + li] * dp[j][it][r];
-            acc += __shfl_xor(acc, 16, kWave);
-            acc += __shfl_xor(acc, 32, kWave);
+            acc = xrow_sum(acc);
             part[it] = acc;
         }
         if (lg == 0) {

@@ -232,8 +232,7 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_bf16_kernel(
                     x[ft][r] *= sg;
                     mx = fmaxf(mx, x[ft][r]);
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+            mx = xrow_max(mx);
             float sum = 0.f;
 #pragma unroll
             for (int ft = 0; ft < NFT; ++ft)
@@ -242,8 +241,7 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_bf16_kernel(
                     x[ft][r] = fast_exp(x[ft][r] - mx);   // <= 1
                     sum += x[ft][r];
                 }
-            sum += __shfl_xor(sum, 16, kWave);
-            sum += __shfl_xor(sum, 32, kWave);
+            sum = xrow_sum(sum);
             const float inv = 1.0f / sum;
             float lpart = 0.f;   // this sign's share of phi(q) . Z
 #pragma unroll
@@ -260,8 +258,7 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_bf16_kernel(
                 store_split4(pqh + pos, pql + pos, x[ft][0], x[ft][1], x[ft][2], x[ft][3]);
                 if ((ft & 1) == 1) fence();
             }
-            lpart += __shfl_xor(lpart, 16, kWave);
-            lpart += __shfl_xor(lpart, 32, kWave);
+            lpart = xrow_sum(lpart);
             if (lg == 0) rs[t * 4 + (side ? 3 : 0)] = lpart;
             if (side) {
                 // scores of queries t against keys 16 jt + 4 lg + r (log2
@@ -284,8 +281,7 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_bf16_kernel(
                         s[jt][r] = 16 * jt + 4 * lg + r < L ? s[jt][r] * kScaleLog2 : -INFINITY;
                         M = fmaxf(M, s[jt][r]);
                     }
-                M = fmaxf(M, __shfl_xor(M, 16, kWave));
-                M = fmaxf(M, __shfl_xor(M, 32, kWave));   // finite: key 0 is always valid
+                M = xrow_max(M);   // finite: key 0 is always valid
                 float smd = 0.f;
 #pragma unroll
                 for (int jt = 0; jt < 2; ++jt) {
@@ -297,8 +293,7 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_forward_bf16_kernel(
                     store_split4(pph + t * TLD + 16 * jt + 4 * lg, ppl + t * TLD + 16 * jt + 4 * lg, s[jt][0],
                                  s[jt][1], s[jt][2], s[jt][3]);
                 }
-                smd += __shfl_xor(smd, 16, kWave);
-                smd += __shfl_xor(smd, 32, kWave);
+                smd = xrow_sum(smd);
                 if (lg == 0) {
                     rs[t * 4 + 1] = M;
                     rs[t * 4 + 2] = smd;
@@ -671,8 +666,7 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_sweep_bf16_kernel(Tr
                     x[ft][r] *= sg;
                     mx = fmaxf(mx, x[ft][r]);
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+            mx = xrow_max(mx);
             float sum = 0.f;
 #pragma unroll
             for (int ft = 0; ft < NFT; ++ft)
@@ -681,8 +675,7 @@ __global__ __launch_bounds__(kXferThreads, 1) void transfer_sweep_bf16_kernel(Tr
                     x[ft][r] = fast_exp(x[ft][r] - mx);
                     sum += x[ft][r];
                 }
-            sum += __shfl_xor(sum, 16, kWave);
-            sum += __shfl_xor(sum, 32, kWave);
+            sum = xrow_sum(sum);
             const float inv = 1.0f / sum;
 #pragma unroll
             for (int ft = 0; ft < NFT; ++ft) {
