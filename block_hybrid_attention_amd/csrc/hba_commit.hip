@@ -436,6 +436,311 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
     if (zf >= 0 && zf < F) __builtin_nontemporal_store(zacc, Zg + zf);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 inputs, d = 128, more than one 32-token chunk (prefill-sized commits):
+// the chunks are pipelined.  Two workgroups per (request, head), one per
+// state half, four waves each.
+//   * Waves 0-1 (producers) form phi(K) of chunk j + 1 for tokens 0-15 and
+//     16-31 of the chunk while chunk j is folded in: k rows are loaded
+//     straight into MFMA A operands two chunks ahead, W^T (staged through
+//     LDS once) is held in registers for the whole call, and phi goes to LDS
+//     in fp32.
+//   * Waves 2-3 (consumers) each own F/2 rows of this state half in the
+//     MFMA accumulators for the whole call and add phi(K_j)^T V_j on bf16
+//     MFMA, phi split into a bf16 high part and a residual (v is exact).
+//     They also stage V^T of the next chunk (v rows requested two chunks
+//     ahead) and sum Z over each chunk's phi.
+//   * phi and V^T are double-buffered; one barrier per chunk.  About 54 KB
+//     of LDS, so two workgroups share a CU.
+// Measured at B = 8, 2048 tokens: the one-chain form above spent 27% of each
+// chunk waiting for its k and v rows and 36% with waves 2-3 idle while
+// waves 0-1 formed phi; forming phi is the longer of the two roles, so the
+// consumers take V^T and Z.
+template <int F>
+struct ChunkGeom {
+    static constexpr int D = 128;
+    static constexpr int TP = kRows + 8;            // V^T row stride (bf16)
+    static constexpr int PHLD = F + 2;              // phi row stride (floats)
+    static constexpr int vt = 0;                    // [buf][D][TP] bf16, rows in N-tile order
+    static constexpr int vt_buf = D * TP * 2;
+    static constexpr int ph = vt + 2 * vt_buf;      // [buf][32 tokens][PHLD] fp32
+    static constexpr int ph_buf = kRows * PHLD * 4;
+    static constexpr int loop_bytes = ph + 2 * ph_buf;
+    static constexpr int wt_bytes = F * (D + 8) * 2;   // W^T at entry, then the chunk buffers
+    static constexpr int bytes = loop_bytes > wt_bytes ? loop_bytes : wt_bytes;
+    static_assert(ph % 16 == 0, "16-byte aligned buffers");
+};
+
+template <int F>
+__global__ __launch_bounds__(kThreads, 2) void commit_chunks_kernel_bf16(CommitArgs a) {
+    using T = uint16_t;
+    using G = ChunkGeom<F>;
+    constexpr int D = G::D;
+    constexpr int NT = F / 16;          // feature tiles of this half
+    constexpr int KS = D / 32;          // K-steps of the projection
+    constexpr int NE = D / 16;          // N-tiles of the state, paired as in commit_kernel_bf16
+    constexpr int FW = F / 2;           // state rows per consumer wave
+    constexpr int MT = FW / 16;
+    constexpr int WBLK = (D / 8) * (F / 8);
+    static_assert(WBLK % 128 == 0, "W^T staging: whole 8x8 blocks per producer thread");
+
+    __shared__ __attribute__((aligned(16))) char smem[G::bytes];
+    T *wts = reinterpret_cast<T *>(smem);
+
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    // the two state halves of a (request, head) on one XCD, as in commit_kernel_bf16
+    int half, bh;
+    {
+        const int g = (int)blockIdx.x, grp = g >> 4;
+        if ((grp + 1) * 8 <= a.B * a.H) {
+            half = (g >> 3) & 1;
+            bh = grp * 8 + (g & 7);
+        } else {
+            half = g & 1;
+            bh = g >> 1;
+        }
+    }
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int T_ = a.T;
+    int nv = a.n_valid ? a.n_valid[b] : T_;
+    nv = nv < 0 ? 0 : (nv > T_ ? T_ : nv);
+    if (nv == 0) return;   // nothing to fold; the state is left untouched
+    const int64_t slot = a.slot ? (int64_t)a.slot[b] : (int64_t)b;
+    const T *kg = static_cast<const T *>(a.k) + (int64_t)(bh / a.G) * T_ * D;
+    const T *vg = static_cast<const T *>(a.v) + (int64_t)(bh / a.G) * T_ * D;
+    const T *Wg = static_cast<const T *>(a.W) + (int64_t)h * D * F;
+    float *Sg = a.S + ((slot * a.H + h) * (int64_t)(2 * F) + (int64_t)half * F) * D;
+    float *Zg = a.Z + (slot * a.H + h) * (int64_t)(2 * F) + half * F;
+    const int nch = (nv + kRows - 1) / kRows;
+    auto vt_of = [&](int buf) { return reinterpret_cast<T *>(smem + G::vt + buf * G::vt_buf); };
+    auto ph_of = [&](int buf) { return reinterpret_cast<float *>(smem + G::ph + buf * G::ph_buf); };
+
+    // consumers: the old state straight into the accumulators, at entry
+    floatx4 acc[MT][NE];
+    const int f_base = (wave - 2) * FW;
+    if (wave >= 2) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float *p = Sg + (int64_t)(f_base + 16 * mt + 4 * lg + r) * D + 2 * li;
+#pragma unroll
+                for (int q = 0; q < NE / 2; ++q) {
+                    const floatx2 t = __builtin_nontemporal_load(reinterpret_cast<const floatx2 *>(p + 32 * q));
+                    acc[mt][2 * q + 0][r] = t[0];
+                    acc[mt][2 * q + 1][r] = t[1];
+                }
+            }
+    }
+    const int zf = tid - 128;   // consumers: one feature each for Z
+    float zacc = (zf >= 0 && zf < F) ? Zg[zf] : 0.f;
+
+    if (wave < 2) {
+        // W^T into LDS: producer thread tid transposes 8x8 blocks (rows 8 bi..,
+        // columns 8 bf..) of W (the consumers' loads are the state's)
+#pragma unroll
+        for (int blk = tid; blk < WBLK; blk += 128) {
+            const int bf = blk % (F / 8), bi = blk / (F / 8);
+            uint4 wb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wb[e] = *reinterpret_cast<const uint4 *>(Wg + (int64_t)(8 * bi + e) * F + 8 * bf);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                uint32_t w[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    w[j] = __builtin_amdgcn_perm(u4_word(wb[2 * j + 1], c >> 1), u4_word(wb[2 * j], c >> 1), sel);
+                *reinterpret_cast<uint4 *>(wts + wt_off<D>(8 * bf + c, bi)) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+        // ------------------------------------------------------------ producers
+        // k row 16 w + l%16 of a chunk, columns 32 ks + 8 (l/16) ..: the MFMA A
+        // operand of u = k W.  Two register sets: even chunks in kA, odd in kB,
+        // each requested two chunks ahead of its use.
+        uint4 kA[KS], kB[KS];
+        auto request = [&](int j, uint4 (&kin)[KS]) __attribute__((always_inline)) {
+            const int tk = j * kRows + 16 * wave + li;
+            const T *kr = kg + (int64_t)(tk < nv ? tk : nv - 1) * D + 8 * lg;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) kin[ks] = *reinterpret_cast<const uint4 *>(kr + 32 * ks);
+        };
+        // requests past the last chunk read the last valid row again: every
+        // request is unconditional, so the loop's waits count exactly
+        request(0, kA);
+        request(1, kB);
+        __syncthreads();   // W^T staged
+        bf16x8 wreg[KS][NT];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                wreg[ks][nt] = *reinterpret_cast<const bf16x8 *>(wts + wt_off<D>(16 * nt + li, 4 * ks + lg));
+        __syncthreads();   // W^T read: its LDS becomes the chunk buffers
+        // phi of chunk j into buffer j % 2, fp32 [token][feature]; tokens past
+        // the chunk's valid ones get 0
+        auto produce = [&](int j, const uint4 (&kin)[KS]) __attribute__((always_inline)) {
+            const int nrows = nv - j * kRows < kRows ? nv - j * kRows : kRows;
+            floatx4 u[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) u[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 ak = __builtin_bit_cast(bf16x8, kin[ks]);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) u[nt] = mfma_bf16(ak, wreg[ks][nt], u[nt]);
+            }
+            // u[nt][r] = u[token 16 w + 4 lg + r][feature 16 nt + li]; this half
+            // of phi is softmax(sgn u) per token (log2 domain)
+            const float sgn2 = half ? -kLog2e : kLog2e;
+            float mref[4], inv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float m0 = -INFINITY;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    u[nt][r] *= sgn2;
+                    m0 = fmaxf(m0, u[nt][r]);
+                }
+                mref[r] = row16_max(m0);
+                float s0 = 0.f;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) s0 += fast_exp2(u[nt][r] - mref[r]);
+                inv[r] = (16 * wave + 4 * lg + r) < nrows ? 1.0f / row16_sum(s0) : 0.f;
+            }
+            float *phs = ph_of(j & 1);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    phs[(16 * wave + 4 * lg + r) * G::PHLD + 16 * nt + li] = fast_exp2(u[nt][r] - mref[r]) * inv[r];
+        };
+        produce(0, kA);
+        request(2, kA);
+        // chunk j is handed over at the j-th barrier; pairs of chunks per
+        // iteration keep the two register sets static
+        int j = 0;
+#pragma unroll 1
+        for (; j + 2 < nch; j += 2) {
+            __syncthreads();   // chunk j handed over; buffer (j + 1) % 2 is free
+            produce(j + 1, kB);
+            request(j + 3, kB);
+            __syncthreads();   // chunk j + 1 handed over
+            produce(j + 2, kA);
+            request(j + 4, kA);
+        }
+        __syncthreads();       // chunk j (the last or the one before it)
+        if (j + 1 < nch) {
+            produce(j + 1, kB);
+            __syncthreads();   // the last chunk
+        }
+    } else {
+        // ------------------------------------------------------------ consumers
+        // V^T of chunk j into buffer j % 2: thread ct = tid - 128 takes tokens
+        // 4 (ct / 16) .. + 3, columns 8 (ct % 16) .. + 7; row rho of V^T holds
+        // the column that N-tile pair q gives lane l (32 q + 2 l and + 1).
+        // Two register sets, each requested two chunks ahead of its staging.
+        const int ct = tid - 128, cb = ct & 15, tq = ct >> 4;
+        uint4 vA[4], vB[4];
+        auto request_v = [&](int j, uint4 (&vin)[4]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int tv = j * kRows + 4 * tq + e;
+                vin[e] = *reinterpret_cast<const uint4 *>(vg + (int64_t)(tv < nv ? tv : nv - 1) * D + 8 * cb);
+            }
+        };
+        auto stage_v = [&](int j, const uint4 (&vin)[4]) __attribute__((always_inline)) {
+            const int nrows = nv - j * kRows < kRows ? nv - j * kRows : kRows;
+            T *vtb = vt_of(j & 1);
+            uint4 x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool ok = 4 * tq + e < nrows;   // tokens past the valid ones: v = 0
+                x[e] = make_uint4(ok ? vin[e].x : 0u, ok ? vin[e].y : 0u, ok ? vin[e].z : 0u, ok ? vin[e].w : 0u);
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int col = 8 * cb + c;
+                const int rho = (2 * (col >> 5) + (col & 1)) * 16 + ((col & 31) >> 1);
+                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                const uint32_t w0 = __builtin_amdgcn_perm(u4_word(x[1], c >> 1), u4_word(x[0], c >> 1), sel);
+                const uint32_t w1 = __builtin_amdgcn_perm(u4_word(x[3], c >> 1), u4_word(x[2], c >> 1), sel);
+                *reinterpret_cast<uint2 *>(vtb + rho * G::TP + 4 * tq) = make_uint2(w0, w1);
+            }
+        };
+        // Z sums and S += phi^T V for chunk j: A[f][t] = phi_f(k_t) (high +
+        // residual), B[t][col] = v_t[col]
+        auto consume = [&](int j) __attribute__((always_inline)) {
+            const float *phs = ph_of(j & 1);
+            const T *vtb = vt_of(j & 1);
+            if (zf < F) {
+                float zs = 0.f;
+#pragma unroll 8
+                for (int i = 0; i < kRows; ++i) zs += phs[i * G::PHLD + zf];
+                zacc += zs;
+            }
+            bf16x8 bv[NE];
+#pragma unroll
+            for (int nt = 0; nt < NE; ++nt) bv[nt] = *reinterpret_cast<const bf16x8 *>(vtb + (16 * nt + li) * G::TP + 8 * lg);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                bf16x8 ah, al;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const float x = phs[(8 * lg + t) * G::PHLD + f_base + 16 * mt + li];
+                    const __bf16 hx = (__bf16)x;
+                    ah[t] = hx;
+                    al[t] = (__bf16)(x - (float)hx);
+                }
+#pragma unroll
+                for (int nt = 0; nt < NE; ++nt) {
+                    acc[mt][nt] = mfma_bf16(ah, bv[nt], acc[mt][nt]);
+                    acc[mt][nt] = mfma_bf16(al, bv[nt], acc[mt][nt]);
+                }
+            }
+        };
+        request_v(0, vA);
+        request_v(1, vB);   // past the last chunk: the last valid row again
+        __syncthreads();    // W^T staged
+        __syncthreads();    // W^T read: V^T of chunk 0 may overwrite it
+        stage_v(0, vA);
+        request_v(2, vA);
+        int j = 0;
+#pragma unroll 1
+        for (; j + 2 < nch; j += 2) {
+            __syncthreads();   // phi and V^T of chunk j are in buffer j % 2
+            stage_v(j + 1, vB);
+            request_v(j + 3, vB);
+            consume(j);
+            __syncthreads();   // phi and V^T of chunk j + 1
+            stage_v(j + 2, vA);
+            request_v(j + 4, vA);
+            consume(j + 1);
+        }
+        __syncthreads();       // chunk j (the last or the one before it)
+        const bool two = j + 1 < nch;
+        if (two) stage_v(j + 1, vB);
+        consume(j);
+        if (two) {
+            __syncthreads();   // the last chunk
+            consume(j + 1);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float *p = Sg + (int64_t)(f_base + 16 * mt + 4 * lg + r) * D + 2 * li;
+#pragma unroll
+                for (int q = 0; q < NE / 2; ++q)
+                    __builtin_nontemporal_store(floatx2{acc[mt][2 * q + 0][r], acc[mt][2 * q + 1][r]},
+                                                reinterpret_cast<floatx2 *>(p + 32 * q));
+            }
+        if (zf < F) __builtin_nontemporal_store(zacc, Zg + zf);
+    }
+}
+
 template <typename T, int D, int F>
 static hipError_t launch_commit_t(const CommitArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)(a.B * a.H));
@@ -443,6 +748,8 @@ static hipError_t launch_commit_t(const CommitArgs &a, hipStream_t stream) {
         const dim3 grid2((unsigned)(2 * a.B * a.H));   // one workgroup per state half
         if (a.T <= kRows)   // one block: phi reuses the LDS of W
             return launch_kernel(commit_kernel_bf16<D, F, false>, grid2, dim3(kThreads), a, stream);
+        if constexpr (D == 128)   // several chunks: the pipelined form
+            return launch_kernel(commit_chunks_kernel_bf16<F>, grid2, dim3(kThreads), a, stream);
         return launch_kernel(commit_kernel_bf16<D, F, true>, grid2, dim3(kThreads), a, stream);
     } else {
         return launch_kernel(commit_kernel<T, D, F>, grid, dim3(kThreads), a, stream);
