@@ -381,7 +381,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
                 mref[r] = row16_max(m0);
                 float s0 = 0.f;
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) s0 += fast_exp2(u[nt][r] - mref[r]);
+                for (int nt = 0; nt < NT; ++nt) {
+                    u[nt][r] = fast_exp2(u[nt][r] - mref[r]);   // u becomes the numerators
+                    s0 += u[nt][r];
+                }
                 const bool ok = (16 * wave + 4 * lg + r) < nrows;   // rows past the end: phi = 0
                 inv[r] = ok ? 1.0f / row16_sum(s0) : 0.f;
             }
@@ -392,7 +395,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
             for (int r = 0; r < 4; ++r) {
                 float *row = phs + (16 * wave + 4 * lg + r) * G::PHLD;
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) row[16 * nt + li] = fast_exp2(u[nt][r] - mref[r]) * inv[r];
+                for (int nt = 0; nt < NT; ++nt) row[16 * nt + li] = u[nt][r] * inv[r];
             }
         }
         __syncthreads();
@@ -607,7 +610,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_chunks_kernel_bf16(CommitA
                 mref[r] = row16_max(m0);
                 float s0 = 0.f;
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) s0 += fast_exp2(u[nt][r] - mref[r]);
+                for (int nt = 0; nt < NT; ++nt) {
+                    u[nt][r] = fast_exp2(u[nt][r] - mref[r]);   // u becomes the numerators
+                    s0 += u[nt][r];
+                }
                 inv[r] = (16 * wave + 4 * lg + r) < nrows ? 1.0f / row16_sum(s0) : 0.f;
             }
             float *phs = ph_of(j & 1);
@@ -615,7 +621,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_chunks_kernel_bf16(CommitA
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    phs[(16 * wave + 4 * lg + r) * G::PHLD + 16 * nt + li] = fast_exp2(u[nt][r] - mref[r]) * inv[r];
+                    phs[(16 * wave + 4 * lg + r) * G::PHLD + 16 * nt + li] = u[nt][r] * inv[r];
         };
         produce(0, kA);
         request(2, kA);
