@@ -440,13 +440,22 @@ def main():
 
     sets = []
     keep_host = None
+    # the prefixes are committed with hba_commit in one call per set (the
+    # pipelined multi-chunk kernel); sets after the first are timed for
+    # context, the first call of the process being excluded
+    pre_ev = []
     for s in range(N_SETS):
         gs = wl.generator(c.seed * 1000 + s, dev)
         pk = wl.normal((B, H, Pmax, d), 1.0, c.dtype, gs, dev)
         pv = wl.normal((B, H, Pmax, d), 1.0, c.dtype, gs, dev)
         S = torch.zeros((B, H, 2 * F, d), device=dev)
         Z = torch.zeros((B, H, 2 * F), device=dev)
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        ev[0].record()
         hba.commit(pk, pv, W, S, Z, n_valid=plen.to(dev))
+        ev[1].record()
+        if s > 0:
+            pre_ev.append(ev)
         q, k, v = wl.block_qkv(B, H, L, d, c.dtype, gs, dev)
         out = torch.empty((B, H, L, d), device=dev)
         if s == 0 and not args.no_cpu_baseline:
@@ -455,6 +464,10 @@ def main():
         del pk, pv
         sets.append((q, k, v, S, Z, out))
     torch.cuda.synchronize()
+
+    prefix_us = statistics.mean(a_.elapsed_time(b_) for a_, b_ in pre_ev) * 1e3 if pre_ev else None
+    prefix_tokens = int(plen.sum())
+    prefix_bytes = prefix_tokens * H * 2 * d * 2 + B * H * 2 * F * (d + 1) * 4 * 2
 
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
@@ -568,7 +581,13 @@ def main():
                        "step_commit_algorithmic_bytes": sc_bytes,
                        "feature_map_us": fm_ms * 1e3,
                        "feature_map_GBps": fm_bytes / (fm_ms * 1e-3) / 1e9,
-                       "feature_map_algorithmic_bytes": fm_bytes},
+                       "feature_map_algorithmic_bytes": fm_bytes,
+                       "prefix_commit_us": prefix_us,
+                       "prefix_commit_tokens": prefix_tokens,
+                       "prefix_commit_M_tokens_per_s": (prefix_tokens / (prefix_us * 1e-6) / 1e6
+                                                        if prefix_us else None),
+                       "prefix_commit_GBps": prefix_bytes / (prefix_us * 1e-6) / 1e9 if prefix_us else None,
+                       "prefix_commit_algorithmic_bytes": prefix_bytes},
     }
     print(json.dumps(line), flush=True)
 

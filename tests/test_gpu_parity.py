@@ -506,3 +506,42 @@ def test_commit_one_block_serving_shapes(B, T, F, Hkv):
     errs = dict(S=state_rel(S, Sr), Z=state_rel(Z[..., None], Zr[..., None]))
     report(f"one-block commit B={B} T={T} F={F} Hkv={Hkv}", **errs)
     check(errs, dt)
+
+
+@pytest.mark.parametrize("B,T,F,Hkv,nvs", [
+    (12, 192, 128, 16, [0, 1, 32, 33, 64, 65, 96, 97, 128, 160, 191, 192]),
+    (12, 192, 64, 4, [192, 191, 160, 128, 97, 96, 65, 64, 33, 32, 1, 0]),
+    (4, 2048, 128, 16, [2048, 2047, 1025, 33]),
+])
+def test_commit_multichunk_pipeline(B, T, F, Hkv, nvs):
+    """The pipelined bf16 commit (more than one 32-token chunk, d = 128): every
+    chunk count from 0 to T/32 over the requests, both parities of the
+    two-chunk loop and its one-chunk tail, a token count that is not a
+    multiple of 32, grouped key/value heads and a slot map into a larger
+    pool; every state against the oracle, untouched slots and n_valid = 0
+    pairs bitwise."""
+    H, d = 16, 128
+    dt = torch.bfloat16
+    g = gen(8800 + B + T + F + Hkv)
+    W = wl.feature_weights(H, d, F, dt, g, DEV)
+    k, v = wl.normal((B, Hkv, T, d), 1, dt, g, DEV), wl.normal((B, Hkv, T, d), 1, dt, g, DEV)
+    slots = B + 3
+    slot = torch.randperm(slots, generator=g, device=DEV)[:B].to(torch.int32)
+    n_valid = torch.tensor(nvs, dtype=torch.int32, device=DEV)
+    S, Z = zeros_pool(slots, H, F, d)
+    S += 0.05 * torch.randn(S.shape, generator=g, device=DEV)
+    Z += torch.rand(Z.shape, generator=g, device=DEV)
+    S0, Z0 = S.clone(), Z.clone()
+    hba.commit(k, v, W, S, Z, n_valid=n_valid, slot=slot)
+    Sr, Zr = oracle.commit(S0, Z0, k, v, W, n_valid=n_valid, slot=slot)
+    used = set(slot.tolist())
+    for sl in range(slots):
+        if sl not in used:
+            assert torch.equal(S[sl], S0[sl]) and torch.equal(Z[sl], Z0[sl])
+    for b in range(B):
+        if nvs[b] == 0:
+            sl = int(slot[b])
+            assert torch.equal(S[sl], S0[sl]) and torch.equal(Z[sl], Z0[sl])
+    errs = dict(S=state_rel(S, Sr), Z=state_rel(Z[..., None], Zr[..., None]))
+    report(f"multi-chunk commit B={B} T={T} F={F} Hkv={Hkv}", **errs)
+    check(errs, dt)
