@@ -447,14 +447,15 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
 //     16-31 of the chunk while chunk j is folded in: k rows are loaded
 //     straight into MFMA A operands two chunks ahead, W^T (staged through
 //     LDS once) is held in registers for the whole call, and phi goes to LDS
-//     in fp32.
+//     in fp32, transposed ([feature][token]).
 //   * Waves 2-3 (consumers) each own F/2 rows of this state half in the
 //     MFMA accumulators for the whole call and add phi(K_j)^T V_j on bf16
 //     MFMA, phi split into a bf16 high part and a residual (v is exact).
 //     They also stage V^T of the next chunk (v rows requested two chunks
-//     ahead) and sum Z over each chunk's phi.
-//   * phi and V^T are double-buffered; one barrier per chunk.  About 54 KB
-//     of LDS, so two workgroups share a CU.
+//     ahead) and take Z's token sums from the phi values they load as MFMA
+//     operands.
+//   * phi and V^T are double-buffered; one barrier per chunk.  60 KB of
+//     LDS, so two workgroups share a CU.
 // Measured at B = 8, 2048 tokens: the one-chain form above spent 27% of each
 // chunk waiting for its k and v rows and 36% with waves 2-3 idle while
 // waves 0-1 formed phi; forming phi is the longer of the two roles, so the
@@ -463,11 +464,13 @@ template <int F>
 struct ChunkGeom {
     static constexpr int D = 128;
     static constexpr int TP = kRows + 8;            // V^T row stride (bf16)
-    static constexpr int PHLD = F + 2;              // phi row stride (floats)
+    // phi^T row stride (floats): 10 16-byte chunks, so that 16 lanes on 16
+    // rows at one chunk each hit distinct banks
+    static constexpr int PTLD = kRows + 8;
     static constexpr int vt = 0;                    // [buf][D][TP] bf16, rows in N-tile order
     static constexpr int vt_buf = D * TP * 2;
-    static constexpr int ph = vt + 2 * vt_buf;      // [buf][32 tokens][PHLD] fp32
-    static constexpr int ph_buf = kRows * PHLD * 4;
+    static constexpr int ph = vt + 2 * vt_buf;      // phi^T [buf][F features][PTLD] fp32
+    static constexpr int ph_buf = F * PTLD * 4;
     static constexpr int loop_bytes = ph + 2 * ph_buf;
     static constexpr int wt_bytes = F * (D + 8) * 2;   // W^T at entry, then the chunk buffers
     static constexpr int bytes = loop_bytes > wt_bytes ? loop_bytes : wt_bytes;
@@ -537,8 +540,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_chunks_kernel_bf16(CommitA
                 }
             }
     }
-    const int zf = tid - 128;   // consumers: one feature each for Z
-    float zacc = (zf >= 0 && zf < F) ? Zg[zf] : 0.f;
+    // consumers: Z of rows f_base + 16 mt + l%16, kept (and stored) by lanes l < 16
+    float zacc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) zacc[mt] = (wave >= 2 && lg == 0) ? Zg[f_base + 16 * mt + li] : 0.f;
 
     if (wave < 2) {
         // W^T into LDS: producer thread tid transposes 8x8 blocks (rows 8 bi..,
@@ -582,8 +587,9 @@ __global__ __launch_bounds__(kThreads, 2) void commit_chunks_kernel_bf16(CommitA
             for (int nt = 0; nt < NT; ++nt)
                 wreg[ks][nt] = *reinterpret_cast<const bf16x8 *>(wts + wt_off<D>(16 * nt + li, 4 * ks + lg));
         __syncthreads();   // W^T read: its LDS becomes the chunk buffers
-        // phi of chunk j into buffer j % 2, fp32 [token][feature]; tokens past
-        // the chunk's valid ones get 0
+        // phi of chunk j into buffer j % 2, fp32 [feature][token] (a lane's
+        // four tokens of one feature are one 16-byte write); tokens past the
+        // chunk's valid ones get 0
         auto produce = [&](int j, const uint4 (&kin)[KS]) __attribute__((always_inline)) {
             const int nrows = nv - j * kRows < kRows ? nv - j * kRows : kRows;
             floatx4 u[NT];
@@ -616,12 +622,11 @@ __global__ __launch_bounds__(kThreads, 2) void commit_chunks_kernel_bf16(CommitA
                 }
                 inv[r] = (16 * wave + 4 * lg + r) < nrows ? 1.0f / row16_sum(s0) : 0.f;
             }
-            float *phs = ph_of(j & 1);
+            float *phs = ph_of(j & 1) + li * G::PTLD + 16 * wave + 4 * lg;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    phs[(16 * wave + 4 * lg + r) * G::PHLD + 16 * nt + li] = u[nt][r] * inv[r];
+                *reinterpret_cast<float4 *>(phs + 16 * nt * G::PTLD) =
+                    make_float4(u[nt][0] * inv[0], u[nt][1] * inv[1], u[nt][2] * inv[2], u[nt][3] * inv[3]);
         };
         produce(0, kA);
         request(2, kA);
@@ -676,35 +681,33 @@ __global__ __launch_bounds__(kThreads, 2) void commit_chunks_kernel_bf16(CommitA
                 *reinterpret_cast<uint2 *>(vtb + rho * G::TP + 4 * tq) = make_uint2(w0, w1);
             }
         };
-        // Z sums and S += phi^T V for chunk j: A[f][t] = phi_f(k_t) (high +
-        // residual), B[t][col] = v_t[col]
+        // S += phi^T V for chunk j: A[f][t] = phi_f(k_t) (high + residual),
+        // B[t][col] = v_t[col]; the A values also give Z's token sums
         auto consume = [&](int j) __attribute__((always_inline)) {
-            const float *phs = ph_of(j & 1);
+            const float *phs = ph_of(j & 1) + (f_base + li) * G::PTLD + 8 * lg;
             const T *vtb = vt_of(j & 1);
-            if (zf < F) {
-                float zs = 0.f;
-#pragma unroll 8
-                for (int i = 0; i < kRows; ++i) zs += phs[i * G::PHLD + zf];
-                zacc += zs;
-            }
             bf16x8 bv[NE];
 #pragma unroll
             for (int nt = 0; nt < NE; ++nt) bv[nt] = *reinterpret_cast<const bf16x8 *>(vtb + (16 * nt + li) * G::TP + 8 * lg);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
+                const float4 x0 = *reinterpret_cast<const float4 *>(phs + 16 * mt * G::PTLD);
+                const float4 x1 = *reinterpret_cast<const float4 *>(phs + 16 * mt * G::PTLD + 4);
+                const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
                 bf16x8 ah, al;
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
-                    const float x = phs[(8 * lg + t) * G::PHLD + f_base + 16 * mt + li];
-                    const __bf16 hx = (__bf16)x;
+                    const __bf16 hx = (__bf16)xs[t];
                     ah[t] = hx;
-                    al[t] = (__bf16)(x - (float)hx);
+                    al[t] = (__bf16)(xs[t] - (float)hx);
                 }
 #pragma unroll
                 for (int nt = 0; nt < NE; ++nt) {
                     acc[mt][nt] = mfma_bf16(ah, bv[nt], acc[mt][nt]);
                     acc[mt][nt] = mfma_bf16(al, bv[nt], acc[mt][nt]);
                 }
+                // tokens 8 (l/16) .. + 7 of row f_base + 16 mt + l%16, then all 32
+                zacc[mt] += xrow_sum(((xs[0] + xs[1]) + (xs[2] + xs[3])) + ((xs[4] + xs[5]) + (xs[6] + xs[7])));
             }
         };
         request_v(0, vA);
@@ -743,7 +746,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_chunks_kernel_bf16(CommitA
                     __builtin_nontemporal_store(floatx2{acc[mt][2 * q + 0][r], acc[mt][2 * q + 1][r]},
                                                 reinterpret_cast<floatx2 *>(p + 32 * q));
             }
-        if (zf < F) __builtin_nontemporal_store(zacc, Zg + zf);
+        if (lg == 0) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) __builtin_nontemporal_store(zacc[mt], Zg + f_base + 16 * mt + li);
+        }
     }
 }
 
