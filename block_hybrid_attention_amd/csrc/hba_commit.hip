@@ -199,16 +199,21 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(CommitArgs a) {
 //     128-byte row segment (measured against 8 consecutive columns per lane,
 //     two 16-byte accesses at a 32-byte stride: 128 -> 113 us at B = 128,
 //     35.0 -> 31.1 us at B = 32, bitwise the same states).
-//   * Waves 2-3 sum phi over tokens for Z in fp32, one feature per thread.
+//   * phi goes to LDS transposed ([feature][token]): the producers write a
+//     lane's four tokens of one feature at once, every wave reads a state
+//     row's eight tokens as its MFMA operand in two 16-byte loads, and sums
+//     them for Z.
 template <int D, int F, bool kResidentW>
 struct CommitGeomBf16 {
     using P = ProjGeom<uint16_t, D, F>;
     static constexpr int TP = kRows + 8;         // V^T row stride (bf16): tokens + pad
-    static constexpr int PHLD = F + 2;           // phi-half row stride (floats)
+    // phi^T [F features][PTLD] fp32: 10 16-byte chunks per row, so that 16
+    // lanes on 16 rows at one chunk each hit distinct banks
+    static constexpr int PTLD = kRows + 8;
     static constexpr int k_off = 0;
     static constexpr int v_off = P::x_bytes;
     static constexpr int w_off = v_off + D * TP * 2;
-    static constexpr int phi_bytes = kRows * PHLD * 4;
+    static constexpr int phi_bytes = F * PTLD * 4;
     static constexpr int phi_off = kResidentW ? w_off + P::w_bytes : w_off;
     static constexpr int wregion = kResidentW ? P::w_bytes + phi_bytes
                                               : (P::w_bytes > phi_bytes ? P::w_bytes : phi_bytes);
@@ -351,8 +356,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
             }
     };
     if constexpr (kResidentW) load_state();
-    const int zf = tid - 128;   // waves 2-3: one feature each for the Z sums
-    float zacc = (zf >= 0 && zf < F) ? Zg[zf] : 0.f;
+    // Z of rows f_base + 16 mt + l%16, kept (and stored) by lanes l < 16
+    float zacc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) zacc[mt] = lg == 0 ? Zg[f_base + 16 * mt + li] : 0.f;
 
 #pragma unroll 1
     for (int t0 = 0; t0 < nv; t0 += kRows) {
@@ -391,31 +398,30 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
         }
         __syncthreads();   // k tile and W reads done (phi may reuse W's LDS)
         if (wave < 2) {
+            // phi^T: a lane's four tokens of feature 16 nt + l%16 in one write
+            float *pt = phs + li * G::PTLD + 16 * wave + 4 * lg;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float *row = phs + (16 * wave + 4 * lg + r) * G::PHLD;
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) row[16 * nt + li] = u[nt][r] * inv[r];
-            }
+            for (int nt = 0; nt < NT; ++nt)
+                *reinterpret_cast<float4 *>(pt + 16 * nt * G::PTLD) =
+                    make_float4(u[nt][0] * inv[0], u[nt][1] * inv[1], u[nt][2] * inv[2], u[nt][3] * inv[3]);
         }
         __syncthreads();
-        if (zf >= 0 && zf < F) {
-            float zs = 0.f;
-#pragma unroll 8
-            for (int i = 0; i < kRows; ++i) zs += phs[i * G::PHLD + zf];
-            zacc += zs;
-        }
-        // S += phi^T V on bf16 MFMA: A[f][t] = phi_f(k_t) (high + residual), B[t][col] = v_t[col]
+        // S += phi^T V on bf16 MFMA: A[f][t] = phi_f(k_t) (high + residual),
+        // B[t][col] = v_t[col]; the A values also give Z's token sums
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
+            const float *pa = phs + (f_base + 16 * mt + li) * G::PTLD + 8 * lg;
+            const float4 x0 = *reinterpret_cast<const float4 *>(pa);
+            const float4 x1 = *reinterpret_cast<const float4 *>(pa + 4);
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
             bf16x8 ah, al;
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const float x = phs[(8 * lg + t) * G::PHLD + f_base + 16 * mt + li];
-                const __bf16 hx = (__bf16)x;
+                const __bf16 hx = (__bf16)xs[t];
                 ah[t] = hx;
-                al[t] = (__bf16)(x - (float)hx);
+                al[t] = (__bf16)(xs[t] - (float)hx);
             }
+            zacc[mt] += xrow_sum(((xs[0] + xs[1]) + (xs[2] + xs[3])) + ((xs[4] + xs[5]) + (xs[6] + xs[7])));
 #pragma unroll
             for (int nt = 0; nt < NE; ++nt) {
                 const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(vt + (16 * nt + li) * G::TP + 8 * lg);
@@ -436,7 +442,10 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
                 __builtin_nontemporal_store(floatx2{acc[mt][2 * q + 0][r], acc[mt][2 * q + 1][r]},
                                             reinterpret_cast<floatx2 *>(p + 32 * q));
         }
-    if (zf >= 0 && zf < F) __builtin_nontemporal_store(zacc, Zg + zf);
+    if (lg == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) __builtin_nontemporal_store(zacc[mt], Zg + f_base + 16 * mt + li);
+    }
 }
 
 // ---------------------------------------------------------------------------
