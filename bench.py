@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --comparator     # hybrid step vs full softmax over P-token caches
     python bench.py --decode-loop    # B=32 decode loop: 8 steps + 1 commit per block
+    python bench.py --commit-sweep   # whole-prefix commits (pipelined kernel), B=8..128
 
 Workload (one hybrid layer): 128 requests, 16 heads, head_dim 128, F = 128
 (phi dim 256), active block 32 tokens, bf16 q/k/v/W ~ N(0,1) / N(0,1/d), fp32
@@ -223,6 +224,41 @@ def transfer_bench(args, torch, hba, wl, dev):
                       "issued_frac_of_bf16_mfma_peak": issued / (ms * 1e-3) / 1e12 / 2500.0}), flush=True)
 
 
+def commit_sweep(args, torch, hba, wl, dev):
+    """hba_commit of whole prefixes in one call (bf16, H=16, d=F=128): the
+    pipelined multi-chunk kernel.  Shapes: the 2048-token prefix of the
+    B = 8 workload, and 512, 256 and 2048 tokens at B = 32 and 128.  Each
+    call starts from its own state set (two or more rotate, > 600 MB in all
+    when they fit); the state is read and written once, k and v read once."""
+    H, d, F = 16, 128, 128
+    rows = []
+    for B, T in ((8, 2048), (32, 512), (128, 256), (128, 2048)):
+        g = wl.generator(41 + B + T, dev)
+        W = wl.feature_weights(H, d, F, torch.bfloat16, g, dev)
+        k = wl.normal((B, H, T, d), 1.0, torch.bfloat16, g, dev)
+        v = wl.normal((B, H, T, d), 1.0, torch.bfloat16, g, dev)
+        per_set = B * H * (2 * F * d + 2 * F) * 4
+        nsets = max(2, min(8, -(-600_000_000 // per_set)))
+        sets = [(torch.zeros((B, H, 2 * F, d), device=dev), torch.zeros((B, H, 2 * F), device=dev))
+                for _ in range(nsets)]
+        it = [0]
+
+        def fn():
+            S, Z = sets[it[0] % nsets]
+            it[0] += 1
+            hba.commit(k, v, W, S, Z)
+
+        n = max(4, min(args.steps, 40 if T <= 512 else 10))
+        ms = _time_launches(torch, fn, 2, n, torch.cuda.current_stream())
+        nb = commit_bytes(B, H, T, d, F)
+        rows.append({"batch": B, "tokens": T, "us": ms * 1e3, "M_tokens_per_s": B * T / (ms * 1e-3) / 1e6,
+                     "TBps": nb / (ms * 1e-3) / 1e12, "algorithmic_bytes": nb, "state_sets": nsets})
+        print(json.dumps({"mode": "commit_sweep", **rows[-1]}), flush=True)
+        del k, v, sets
+        torch.cuda.empty_cache()
+    return rows
+
+
 def batch_sweep(args, torch, hba, wl, dev):
     """hba_step (bf16, H=16, d=F=128, L=32) over batch sizes, with enough
     rotating state sets (> 600 MB) that the 256 MB Infinity Cache holds none
@@ -396,6 +432,8 @@ def main():
                     help="time stage-1 attention transfer (loss, dW, dalpha) at 16 x 16 heads x 2048 tokens")
     ap.add_argument("--batch-sweep", action="store_true",
                     help="time hba_step over batch sizes (--batch, default 16..192) and fit fixed + marginal cost")
+    ap.add_argument("--commit-sweep", action="store_true",
+                    help="hba_commit of whole prefixes (8 x 2048 .. 128 x 2048 tokens)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel (torch.neg) "
                          "10 times, to calibrate HBM byte counters")
@@ -429,6 +467,8 @@ def main():
         return decode_loop(args, torch, hba, wl, dev)
     if args.transfer:
         return transfer_bench(args, torch, hba, wl, dev)
+    if args.commit_sweep:
+        return commit_sweep(args, torch, hba, wl, dev)
     if args.batch_sweep:
         return batch_sweep(args, torch, hba, wl, dev)
     c = wl.serving_b128()
