@@ -762,13 +762,221 @@ __global__ __launch_bounds__(kThreads, 2) void commit_chunks_kernel_bf16(CommitA
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 inputs, d = 128, one block (at most 32 tokens): one workgroup of four
+// waves per (request, head), as the fused step + commit.  Wave w owns state
+// columns 32 w .. +31 (two per lane) of all 2F rows and requests its whole
+// column slice before the prologue.  Wave w forms phi of sign w / 2 for
+// tokens 16 (w mod 2) .. +15 (u = K W, so a lane holds four consecutive
+// tokens of one feature) and writes phi(K)^T to LDS as a bf16 high part and
+// residual; the stream then adds dS = phi(K)^T V, whose A rows are taken in
+// the order that makes dS land in the lanes and registers holding each
+// chunk, and stores S + dS in place.  k and v are read once per (request,
+// head), and u once per sign.
+template <int F>
+struct BlockGeom {
+    static constexpr int D = 128;
+    using P = ProjGeom<uint16_t, D, F>;
+    static constexpr int KT = kRows + 8;                  // phi(K)^T row stride (bf16)
+    static constexpr int k_off = 0;                       // k rows, then (after the projection) phi(K)^T
+    static constexpr int w_off = P::x_bytes;              // W^T
+    static constexpr int in_bytes = P::x_bytes + P::w_bytes;
+    static constexpr int kt_bytes = 2 * (2 * F) * KT * 2; // hi rows [2F][KT], then lo rows
+    static constexpr int r1 = in_bytes > kt_bytes ? in_bytes : kt_bytes;
+    static constexpr int zk_off = r1;                     // token sums [2 token tiles][2F]
+    static constexpr int bytes = zk_off + 2 * 2 * F * 4;
+};
+
+template <int F>
+__global__ __launch_bounds__(kThreads, 2) void commit_block_kernel_bf16(CommitArgs a) {
+    using T = uint16_t;
+    using G = BlockGeom<F>;
+    using P = typename G::P;
+    constexpr int D = G::D;
+    constexpr int NCH = 2 * F / 32;   // 32-row chunks of the state, all held by every wave
+    // chunks requested at entry, then after the staging barrier; the rest
+    // once phi(K) is formed (with the whole slice in flight through the
+    // prologue, the state spilled)
+    constexpr int RING = 2;
+    constexpr int PRE = NCH / 2 > RING ? NCH / 2 : NCH;
+    constexpr int NT = F / 16;
+    constexpr int KS = D / 32;
+
+    __shared__ __attribute__((aligned(16))) char smem[G::bytes];
+    T *ks = reinterpret_cast<T *>(smem + G::k_off);
+    T *ws = reinterpret_cast<T *>(smem + G::w_off);
+    T *Khi = reinterpret_cast<T *>(smem + G::k_off);
+    T *Klo = Khi + 2 * F * G::KT;
+    float *zk = reinterpret_cast<float *>(smem + G::zk_off);
+
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int bh = (int)blockIdx.x;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int T_ = a.T;
+    int nv = a.n_valid ? a.n_valid[b] : T_;
+    nv = nv < 0 ? 0 : (nv > T_ ? T_ : nv);
+    if (nv == 0) return;   // nothing to fold; the state is left untouched
+    const int64_t slot = a.slot ? (int64_t)a.slot[b] : (int64_t)b;
+    const T *kg = static_cast<const T *>(a.k) + (int64_t)(bh / a.G) * T_ * D;
+    const T *vg = static_cast<const T *>(a.v) + (int64_t)(bh / a.G) * T_ * D;
+    const T *Wg = static_cast<const T *>(a.W) + (int64_t)h * D * F;
+    float *Sg = a.S + (slot * a.H + h) * (int64_t)(2 * F) * D;
+    float *Zg = a.Z + (slot * a.H + h) * (int64_t)(2 * F);
+
+    // 1. k rows (rows past n_valid read as zero), W and the block values;
+    //    then the ring head of the state
+    RowChunks<T, D> kc;
+    WChunks<T, D, F> wc;
+    load_rows<T, D>(kg, D, nv, kc);
+    load_w<T, D, F>(Wg, wc);
+    const int c0 = 32 * wave + 2 * li;
+    uint32_t vw[8];   // tokens 8 lg + t, columns c0 and c0 + 1 (rows past n_valid repeat row nv - 1; their phi is 0)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int j = 8 * lg + t;
+        vw[t] = *reinterpret_cast<const uint32_t *>(vg + (j < nv ? j : nv - 1) * D + c0);
+    }
+    float sreg[NCH][8][2];
+    // 32-bit element offsets from the (uniform) state base: 64-bit lane
+    // addresses for every chunk row, formed ahead, took the registers the
+    // state needs
+    const int lofs = 8 * lg * D + c0;
+    auto load_chunk = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const floatx2 v2 = __builtin_nontemporal_load(reinterpret_cast<const floatx2 *>(Sg + (lofs + (32 * c + t) * D)));
+            sreg[c][t][0] = v2[0];
+            sreg[c][t][1] = v2[1];
+        }
+    };
+#pragma unroll
+    for (int c = 0; c < RING; ++c) load_chunk(c);
+    store_rows<T, D, F>(kc, ks);
+    store_w<T, D, F>(wc, ws);
+    __syncthreads();
+#pragma unroll
+    for (int c = RING; c < PRE; ++c) load_chunk(c);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. u = K W for tokens 16 g .. +15: acc[m][r] = u[token 16 g + 4(l/16) + r][feature 16m + l%16]
+    const int g = wave & 1, half = wave >> 1;
+    floatx4 acc[NT];
+#pragma unroll
+    for (int m = 0; m < NT; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks_ = 0; ks_ < KS; ++ks_) {
+        const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(ks + (16 * g + li) * P::XLD + 32 * ks_ + 8 * lg);
+#pragma unroll
+        for (int m = 0; m < NT; ++m) {
+            const bf16x8 bw = *reinterpret_cast<const bf16x8 *>(ws + wt_off<D>(16 * m + li, 4 * ks_ + lg));
+            acc[m] = mfma_bf16(ak, bw, acc[m]);
+        }
+        // one K-step's operands at a time: with the whole state slice in
+        // flight, operands read ahead for every K-step spilled the state
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();   // k and W^T are dead: phi(K)^T takes their LDS
+
+    // 3. this wave's sign of phi(k_t), features half F + 16m + l%16; tokens
+    //    past n_valid get phi = 0
+    {
+        const float sgn2 = half ? -kLog2e : kLog2e;
+        const int t0 = 16 * g + 4 * lg;
+        float mx[4], is[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float m0 = -INFINITY;
+#pragma unroll
+            for (int m = 0; m < NT; ++m) {
+                acc[m][r] *= sgn2;
+                m0 = fmaxf(m0, acc[m][r]);
+            }
+            mx[r] = row16_max(m0);   // over the 16 lanes holding this token's features
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float s0 = 0.f;
+#pragma unroll
+            for (int m = 0; m < NT; ++m) {
+                acc[m][r] = fast_exp2(acc[m][r] - mx[r]);
+                s0 += acc[m][r];
+            }
+            is[r] = t0 + r < nv ? 1.0f / row16_sum(s0) : 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < NT; ++m) {
+            const int f = half * F + 16 * m + li;
+            const float e0 = acc[m][0] * is[0], e1 = acc[m][1] * is[1], e2 = acc[m][2] * is[2], e3 = acc[m][3] * is[3];
+            uint32_t hw[2], lw[2];
+            split_pk_bf16(e0, e1, hw[0], lw[0]);
+            split_pk_bf16(e2, e3, hw[1], lw[1]);
+            *reinterpret_cast<uint2 *>(Khi + f * G::KT + t0) = make_uint2(hw[0], hw[1]);
+            *reinterpret_cast<uint2 *>(Klo + f * G::KT + t0) = make_uint2(lw[0], lw[1]);
+            float zt = (e0 + e1) + (e2 + e3);   // this lane's four tokens
+            zt = xrow_sum(zt);
+            if (lg == 0) zk[g * 2 * F + f] = zt;
+        }
+    }
+    __syncthreads();
+
+    // 4. the stream: S + phi(K)^T V, stored in place (the old Z and the
+    //    rest of the state are requested first)
+    const float zold = Zg[tid % (2 * F)];
+#pragma unroll
+    for (int c = PRE; c < NCH; ++c) load_chunk(c);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 bv[2];
+    {
+        uint32_t p0[4], p1[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            p0[j] = __builtin_amdgcn_perm(vw[2 * j + 1], vw[2 * j], 0x05040100u);
+            p1[j] = __builtin_amdgcn_perm(vw[2 * j + 1], vw[2 * j], 0x07060302u);
+        }
+        bv[0] = __builtin_bit_cast(bf16x8, make_uint4(p0[0], p0[1], p0[2], p0[3]));
+        bv[1] = __builtin_bit_cast(bf16x8, make_uint4(p1[0], p1[1], p1[2], p1[3]));
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        // dS tile mt, row 4(l/16) + r = chunk row 8(l/16) + 4 mt + r: the A
+        // operand row of lane l%16 = 4 g' + r' is state row 32c + 8g' + 4mt + r'
+        const int frow = 32 * c + 8 * (li >> 2) + (li & 3);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const bf16x8 kh = *reinterpret_cast<const bf16x8 *>(Khi + (frow + 4 * mt) * G::KT + 8 * lg);
+            const bf16x8 kl = *reinterpret_cast<const bf16x8 *>(Klo + (frow + 4 * mt) * G::KT + 8 * lg);
+            floatx4 ds[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                ds[e] = mfma_bf16(kh, bv[e], floatx4{0.f, 0.f, 0.f, 0.f});
+                ds[e] = mfma_bf16(kl, bv[e], ds[e]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const floatx2 o2 = {sreg[c][4 * mt + r][0] + ds[0][r], sreg[c][4 * mt + r][1] + ds[1][r]};
+                __builtin_nontemporal_store(o2, reinterpret_cast<floatx2 *>(Sg + (lofs + (32 * c + 4 * mt + r) * D)));
+            }
+        }
+        // one chunk at a time: scheduled across chunks, the dS tiles of all
+        // of them were formed ahead of the stores and spilled
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // 5. Z += sum_t phi(k_t)
+    if (tid < 2 * F) __builtin_nontemporal_store(zold + zk[tid] + zk[2 * F + tid], Zg + tid);
+}
+
 template <typename T, int D, int F>
 static hipError_t launch_commit_t(const CommitArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)(a.B * a.H));
     if constexpr (sizeof(T) == 2) {
         const dim3 grid2((unsigned)(2 * a.B * a.H));   // one workgroup per state half
-        if (a.T <= kRows)   // one block: phi reuses the LDS of W
+        if (a.T <= kRows) {   // one block
+            if constexpr (D == 128)
+                return launch_kernel(commit_block_kernel_bf16<F>, grid, dim3(kThreads), a, stream);
             return launch_kernel(commit_kernel_bf16<D, F, false>, grid2, dim3(kThreads), a, stream);
+        }
         if constexpr (D == 128)   // several chunks: the pipelined form
             return launch_kernel(commit_chunks_kernel_bf16<F>, grid2, dim3(kThreads), a, stream);
         return launch_kernel(commit_kernel_bf16<D, F, true>, grid2, dim3(kThreads), a, stream);
