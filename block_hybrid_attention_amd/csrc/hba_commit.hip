@@ -4,9 +4,15 @@
 // (state update once a block is committed):
 //   S <- S + sum_t phi(k_t) v_t^T,   Z <- Z + sum_t phi(k_t).
 //
-// One workgroup (4 waves) per (request, head).  The commit is a read-modify-
-// write of the fp32 state (2 x 128 KB at F = d = 128) plus a small
-// contraction Phi^T V (K = tokens).  Design:
+// The commit is a read-modify-write of the fp32 state (2 x 128 KB at
+// F = d = 128) plus a small contraction Phi^T V (K = tokens).  Four kernels:
+//   * commit_kernel: fp32 inputs (described here);
+//   * commit_kernel_bf16: bf16 inputs, one workgroup per state half (d = 64);
+//   * commit_block_kernel_bf16: bf16, d = 128, one block of at most 32
+//     tokens, one workgroup per (request, head);
+//   * commit_chunks_kernel_bf16: bf16, d = 128, several 32-token chunks,
+//     pipelined.
+// fp32 inputs: one workgroup (4 waves) per (request, head).
 //   * The old state is loaded straight into the MFMA accumulators at entry
 //     (wave w owns state rows [w 2F/4, (w+1) 2F/4)), so the contraction
 //     accumulates onto it and the result is stored once: one read and one
