@@ -578,6 +578,36 @@ def main():
     fm_bytes = B * L * H * d * 2 + H * d * F * 2 + B * L * H * 2 * F * 4
     del xq, phi
 
+    # the B = 8 workload (a 2048-token prefix committed in one call, then the
+    # step): the pipelined commit, and the step replayed from a HIP graph of
+    # 20 launches, which takes the host out of a launch this short
+    B8, T8 = 8, 2048
+    g8 = wl.generator(c.seed * 1000 + 99, dev)
+    k8p = wl.normal((B8, H, T8, d), 1.0, c.dtype, g8, dev)
+    v8p = wl.normal((B8, H, T8, d), 1.0, c.dtype, g8, dev)
+    S8 = torch.zeros((B8, H, 2 * F, d), device=dev)
+    Z8 = torch.zeros((B8, H, 2 * F), device=dev)
+    c8_ms = _time_launches(torch, lambda: hba.commit(k8p, v8p, W, S8, Z8), 2, 10, stream)
+    q8, k8, v8 = wl.block_qkv(B8, H, L, d, c.dtype, g8, dev)
+    o8 = torch.empty((B8, H, L, d), device=dev)
+    for _ in range(3):
+        hba.step(q8, k8, v8, W, S8, Z8, out=o8)
+    torch.cuda.synchronize()
+    graph8 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph8):
+        for _ in range(20):
+            hba.step(q8, k8, v8, W, S8, Z8, out=o8)
+    graph8.replay()
+    torch.cuda.synchronize()
+    e8 = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    e8[0].record(stream)
+    for _ in range(5):
+        graph8.replay()
+    e8[1].record(stream)
+    torch.cuda.synchronize()
+    s8_us = e8[0].elapsed_time(e8[1]) / 100 * 1e3
+    del k8p, v8p, graph8
+
     base = None
     if not args.no_cpu_baseline:
         q0, k0, v0 = sets[0][0], sets[0][1], sets[0][2]
@@ -627,7 +657,10 @@ def main():
                        "prefix_commit_M_tokens_per_s": (prefix_tokens / (prefix_us * 1e-6) / 1e6
                                                         if prefix_us else None),
                        "prefix_commit_GBps": prefix_bytes / (prefix_us * 1e-6) / 1e9 if prefix_us else None,
-                       "prefix_commit_algorithmic_bytes": prefix_bytes},
+                       "prefix_commit_algorithmic_bytes": prefix_bytes,
+                       "b8_prefix_commit_us": c8_ms * 1e3,
+                       "b8_prefix_commit_tokens": B8 * T8,
+                       "b8_step_us_graph": s8_us},
     }
     print(json.dumps(line), flush=True)
 
