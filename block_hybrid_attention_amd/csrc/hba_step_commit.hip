@@ -104,11 +104,12 @@ __global__ __launch_bounds__(kThreads, 2) void step_commit_kernel_bf16(StepCommi
     float4 zq = make_float4(0.f, 0.f, 0.f, 0.f);
     if (tid < ZQ) zq = reinterpret_cast<const float4 *>(Zg)[tid];
     const int c0 = 32 * wave + 2 * li;
+    const int lofs = 8 * lg * D + c0;   // 32-bit element offsets from the uniform state base
     float sreg[NCH][8][2];
-    auto load_chunk = [&](int c) {
+    auto load_chunk = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const floatx2 v2 = __builtin_nontemporal_load(reinterpret_cast<const floatx2 *>(Sg + (int64_t)(32 * c + 8 * lg + t) * D + c0));
+            const floatx2 v2 = __builtin_nontemporal_load(reinterpret_cast<const floatx2 *>(Sg + (lofs + (32 * c + t) * D)));
             sreg[c][t][0] = v2[0];
             sreg[c][t][1] = v2[1];
         }
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(kThreads, 2) void step_commit_kernel_bf16(StepCommi
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const floatx2 o2 = {sreg[c][4 * mt + r][0] + ds[0][r], sreg[c][4 * mt + r][1] + ds[1][r]};
-                    __builtin_nontemporal_store(o2, reinterpret_cast<floatx2 *>(Sg + (int64_t)(32 * c + 8 * lg + 4 * mt + r) * D + c0));
+                    __builtin_nontemporal_store(o2, reinterpret_cast<floatx2 *>(Sg + (lofs + (32 * c + 4 * mt + r) * D)));
                 }
             }
         }
