@@ -69,6 +69,16 @@ MUTANTS = {
            f"{_I12}for (int64_t i = i0; i < i0 + L; ++i) {{"),
           (f"/* commit block n */\n{_I12}for (int64_t t = i0; t < i0 + L; ++t) {{",
            f"/* commit block n */\n{_I12}for (int64_t t = i0; 0 && t < i0 + L; ++t) {{")]),
+    19: ("commit folds every token, ignoring n_valid",
+         [("int nv = n_valid ? n_valid[b] : T;", "int nv = T;")]),
+    20: ("commit writes request b's state, ignoring the slot map",
+         [("int64_t s = slot ? slot[b] : b;\n        double *S = S_pool",
+           "int64_t s = b;\n        double *S = S_pool")]),
+    21: ("step reads request b's state, ignoring the slot map",
+         [("int64_t s = slot ? slot[b] : b;\n        const double *S = S_pool",
+           "int64_t s = b;\n        const double *S = S_pool")]),
+    22: ("comparator reads the whole cache, ignoring prefix_len",
+         [("int P = prefix_len ? prefix_len[b] : max_prefix;", "int P = max_prefix;")]),
 }
 
 
