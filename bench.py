@@ -117,6 +117,28 @@ def _time_launches(torch, fn, warmup, iters, stream):
     return e0.elapsed_time(e1) / iters
 
 
+def _time_graph(torch, fn, n, reps, stream):
+    """Mean time per call (ms) of `fn` captured `n` times in one HIP graph and
+    replayed `reps` times between two events: the host is out of the loop,
+    which matters for launches of a few microseconds."""
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(n):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / (n * reps)
+
+
 def comparator_sweep(args, torch, hba, wl, dev, B=128):
     """Full softmax attention over a P-token bf16 KV cache (the layer the
     hybrid replaces) against the hybrid step reading the fixed-size state
@@ -141,13 +163,15 @@ def comparator_sweep(args, torch, hba, wl, dev, B=128):
         n = max(3, min(args.steps, 20 if P >= 16384 else 50))
         cm = _time_launches(torch, lambda: hba.prefix_softmax(q, k, v, Kc, Vc, out=out_c), 2, n, stream)
         hm = _time_launches(torch, lambda: hba.step(q, k, v, W, S, Z, out=out_h), 3, n, stream)
+        hg = _time_graph(torch, lambda: hba.step(q, k, v, W, S, Z, out=out_h), 20, 5, stream)
         kv_bytes = 2 * B * H * P * d * 2
         c_bytes = kv_bytes + 3 * B * H * L * d * 2 + B * H * L * d * 4
         row = {"prefix": P, "comparator_ms": cm,
                "comparator_GBps": c_bytes / (cm * 1e-3) / 1e9,
                "hybrid_ms": hm,
                "hybrid_GBps": step_bytes(B, H, L, d, F) / (hm * 1e-3) / 1e9,
-               "speedup": cm / hm, "comparator_kv_bytes": kv_bytes}
+               "speedup": cm / hm, "comparator_kv_bytes": kv_bytes,
+               "hybrid_graph_ms": hg, "speedup_vs_hybrid_graph": cm / hg}
         ns_auto = hba.prefix_softmax_auto_split(B, H, L, d, P)
         if ns_auto > 1:
             ws = torch.empty(hba.prefix_softmax_workspace_bytes(B, H, L, d, 64) // 4, device=dev)
@@ -162,6 +186,7 @@ def comparator_sweep(args, torch, hba, wl, dev, B=128):
             sm = sweep[ns_auto]
             row.update({"split_auto": ns_auto, "split_ms": sm,
                         "split_GBps": c_bytes / (sm * 1e-3) / 1e9, "split_speedup_vs_hybrid": sm / hm,
+                        "split_speedup_vs_hybrid_graph": sm / hg,
                         "split_sweep_ms": sweep, "split_vs_unsplit_max_row_rel": err})
             del ws
         rows.append(row)
@@ -590,23 +615,8 @@ def main():
     c8_ms = _time_launches(torch, lambda: hba.commit(k8p, v8p, W, S8, Z8), 2, 10, stream)
     q8, k8, v8 = wl.block_qkv(B8, H, L, d, c.dtype, g8, dev)
     o8 = torch.empty((B8, H, L, d), device=dev)
-    for _ in range(3):
-        hba.step(q8, k8, v8, W, S8, Z8, out=o8)
-    torch.cuda.synchronize()
-    graph8 = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph8):
-        for _ in range(20):
-            hba.step(q8, k8, v8, W, S8, Z8, out=o8)
-    graph8.replay()
-    torch.cuda.synchronize()
-    e8 = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    e8[0].record(stream)
-    for _ in range(5):
-        graph8.replay()
-    e8[1].record(stream)
-    torch.cuda.synchronize()
-    s8_us = e8[0].elapsed_time(e8[1]) / 100 * 1e3
-    del k8p, v8p, graph8
+    s8_us = _time_graph(torch, lambda: hba.step(q8, k8, v8, W, S8, Z8, out=o8), 20, 5, stream) * 1e3
+    del k8p, v8p
 
     base = None
     if not args.no_cpu_baseline:
