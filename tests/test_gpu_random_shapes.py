@@ -4,7 +4,8 @@ fp64 oracle.
 Each case draws, from its own seed, an input dtype, head_dim, feature width,
 query heads and a key/value head count dividing them, a batch (some large
 enough that the bf16 d = 128 step runs one workgroup per pair, most small
-enough for its column split), a block length in 1..32, a prefix of 0..100
+enough for its column split; the last cases 24 to 48 requests at 8 to 16
+heads, more pairs than CUs), a block length in 1..32, a prefix of 0..100
 tokens committed in one call (one chunk or several), ragged n_valid with
 zeros, a slot map into a larger pool or none, a gate or none, and a ragged
 comparator prefix with a key split of 1, 2, 3 or 5.  Every case runs, on the
@@ -22,6 +23,7 @@ from parity import check, report, row_rel, state_rel
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 N_CASES = 40
+N_LARGE = 12   # cases N_CASES .. N_CASES + N_LARGE - 1: B = 24..48 at 8, 12 or 16 heads
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -35,8 +37,13 @@ def _library():
 def draw(case):
     r = np.random.default_rng(12_000 + case)
     H = int(r.choice([1, 2, 3, 4, 6, 8, 16]))
+    if case >= N_CASES:   # the large-batch cases: more (request, head) pairs than CUs
+        H = int(r.choice([8, 12, 16]))
     divisors = [x for x in range(1, H + 1) if H % x == 0]
-    B = int(r.integers(1, 25)) if r.random() < 0.8 else int(r.integers(16, 41))
+    if case >= N_CASES:
+        B = int(r.integers(24, 49))
+    else:
+        B = int(r.integers(1, 25)) if r.random() < 0.8 else int(r.integers(16, 41))
     return dict(
         dtype=torch.bfloat16 if r.random() < 0.6 else torch.float32,
         d=int(r.choice([64, 128])), F=int(r.choice([64, 128])), H=H, Hkv=int(r.choice(divisors)), B=B,
@@ -45,7 +52,7 @@ def draw(case):
         n_split=int(r.choice([1, 2, 3, 5])), seed=int(r.integers(1 << 30)))
 
 
-@pytest.mark.parametrize("case", range(N_CASES))
+@pytest.mark.parametrize("case", range(N_CASES + N_LARGE))
 def test_random_shape_all_entry_points(case):
     c = draw(case)
     dt, d, F, H, Hkv, B, L, T, P = (c[k] for k in ("dtype", "d", "F", "H", "Hkv", "B", "L", "T", "P"))
