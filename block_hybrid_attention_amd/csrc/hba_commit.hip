@@ -10,8 +10,8 @@
 //   * commit_kernel_bf16: bf16 inputs, one workgroup per state half (d = 64);
 //   * commit_block_kernel_bf16: bf16, d = 128, one block of at most 32
 //     tokens, one workgroup per (request, head);
-//   * commit_chunks_kernel_bf16: bf16, d = 128, several 32-token chunks,
-//     pipelined.
+//   * commit_chunks_kernel_bf16: bf16, d = 128, several chunks of 32 or 64
+//     tokens, pipelined.
 // fp32 inputs: one workgroup (4 waves) per (request, head).
 //   * The old state is loaded straight into the MFMA accumulators at entry
 //     (wave w owns state rows [w 2F/4, (w+1) 2F/4)), so the contraction
@@ -457,31 +457,35 @@ __global__ __launch_bounds__(kThreads, 2) void commit_kernel_bf16(CommitArgs a) 
 // ---------------------------------------------------------------------------
 // bf16 inputs, d = 128, more than one 32-token chunk (prefill-sized commits):
 // the chunks are pipelined.  Two workgroups per (request, head), one per
-// state half, four waves each.
-//   * Waves 0-1 (producers) form phi(K) of chunk j + 1 for tokens 0-15 and
-//     16-31 of the chunk while chunk j is folded in: k rows are loaded
-//     straight into MFMA A operands two chunks ahead, W^T (staged through
-//     LDS once) is held in registers for the whole call, and phi goes to LDS
-//     in fp32, transposed ([feature][token]).
-//   * Waves 2-3 (consumers) each own F/2 rows of this state half in the
-//     MFMA accumulators for the whole call and add phi(K_j)^T V_j on bf16
-//     MFMA, phi split into a bf16 high part and a residual (v is exact).
-//     They also stage V^T of the next chunk (v rows requested two chunks
-//     ahead) and take Z's token sums from the phi values they load as MFMA
+// state half, with CW producer and CW consumer waves each; a chunk is 16 CW
+// tokens.
+//   * The producers form phi(K) of chunk j + 1, 16 tokens each, while chunk
+//     j is folded in: k rows are loaded straight into MFMA A operands two
+//     chunks ahead, W^T (staged through LDS once) is held in registers for
+//     the whole call, and phi goes to LDS in fp32, transposed
+//     ([feature][token]).
+//   * The consumers each own F/CW rows of this state half in the MFMA
+//     accumulators for the whole call and add phi(K_j)^T V_j on bf16 MFMA,
+//     phi split into a bf16 high part and a residual (v is exact).  They
+//     also stage V^T of the next chunk (v rows requested two chunks ahead)
+//     and take Z's token sums from the phi values they load as MFMA
 //     operands.
-//   * phi and V^T are double-buffered; one barrier per chunk.  60 KB of
-//     LDS, so two workgroups share a CU.
+//   * phi and V^T are double-buffered; one barrier per chunk.  CW = 2: 64 KB
+//     of LDS, two workgroups per CU.  CW = 4: 112 KB, one eight-wave
+//     workgroup per CU, for grids that give each CU at most one workgroup
+//     (the four-wave form would leave each SIMD a single wave).
 // Measured at B = 8, 2048 tokens: the one-chain form above spent 27% of each
 // chunk waiting for its k and v rows and 36% with waves 2-3 idle while
 // waves 0-1 formed phi; forming phi is the longer of the two roles, so the
 // consumers take V^T and Z.
-template <int F>
+template <int F, int CW>
 struct ChunkGeom {
     static constexpr int D = 128;
-    static constexpr int TP = kRows + 8;            // V^T row stride (bf16)
-    // phi^T row stride (floats): 10 16-byte chunks, so that 16 lanes on 16
-    // rows at one chunk each hit distinct banks
-    static constexpr int PTLD = kRows + 8;
+    static constexpr int CT = 16 * CW;              // tokens per chunk
+    // row strides of 6 or 10 16-byte chunks (2 mod 4): the operand reads (16
+    // rows at one chunk each) hit distinct banks
+    static constexpr int TP = CT + 16;              // V^T row stride (bf16)
+    static constexpr int PTLD = CT + 8;             // phi^T row stride (floats)
     static constexpr int vt = 0;                    // [buf][D][TP] bf16, rows in N-tile order
     static constexpr int vt_buf = D * TP * 2;
     static constexpr int ph = vt + 2 * vt_buf;      // phi^T [buf][F features][PTLD] fp32
@@ -489,21 +493,25 @@ struct ChunkGeom {
     static constexpr int loop_bytes = ph + 2 * ph_buf;
     static constexpr int wt_bytes = F * (D + 8) * 2;   // W^T at entry, then the chunk buffers
     static constexpr int bytes = loop_bytes > wt_bytes ? loop_bytes : wt_bytes;
-    static_assert(ph % 16 == 0, "16-byte aligned buffers");
+    static_assert(ph % 16 == 0 && TP >= CT + 8, "16-byte aligned buffers, room for a chunk");
+    static_assert((TP / 8) % 4 == 2 && (PTLD / 4) % 4 == 2, "conflict-free row strides");
 };
 
-template <int F>
-__global__ __launch_bounds__(kThreads, 2) void commit_chunks_kernel_bf16(CommitArgs a) {
+template <int F, int CW>
+__global__ __launch_bounds__(128 * CW, CW == 2 ? 2 : 1) void commit_chunks_kernel_bf16(CommitArgs a) {
     using T = uint16_t;
-    using G = ChunkGeom<F>;
+    using G = ChunkGeom<F, CW>;
     constexpr int D = G::D;
+    constexpr int CT = G::CT;
     constexpr int NT = F / 16;          // feature tiles of this half
     constexpr int KS = D / 32;          // K-steps of the projection
     constexpr int NE = D / 16;          // N-tiles of the state, paired as in commit_kernel_bf16
-    constexpr int FW = F / 2;           // state rows per consumer wave
+    constexpr int FW = F / CW;          // state rows per consumer wave
     constexpr int MT = FW / 16;
+    constexpr int KC = CT / 32;         // K-steps of the contraction per chunk
+    constexpr int NP = 64 * CW;         // threads per role
     constexpr int WBLK = (D / 8) * (F / 8);
-    static_assert(WBLK % 128 == 0, "W^T staging: whole 8x8 blocks per producer thread");
+    static_assert(MT >= 1, "at least one 16-row tile per consumer wave");
 
     __shared__ __attribute__((aligned(16))) char smem[G::bytes];
     T *wts = reinterpret_cast<T *>(smem);
@@ -534,14 +542,14 @@ __global__ __launch_bounds__(kThreads, 2) void commit_chunks_kernel_bf16(CommitA
     const T *Wg = static_cast<const T *>(a.W) + (int64_t)h * D * F;
     float *Sg = a.S + ((slot * a.H + h) * (int64_t)(2 * F) + (int64_t)half * F) * D;
     float *Zg = a.Z + (slot * a.H + h) * (int64_t)(2 * F) + half * F;
-    const int nch = (nv + kRows - 1) / kRows;
+    const int nch = (nv + CT - 1) / CT;
     auto vt_of = [&](int buf) { return reinterpret_cast<T *>(smem + G::vt + buf * G::vt_buf); };
     auto ph_of = [&](int buf) { return reinterpret_cast<float *>(smem + G::ph + buf * G::ph_buf); };
 
     // consumers: the old state straight into the accumulators, at entry
     floatx4 acc[MT][NE];
-    const int f_base = (wave - 2) * FW;
-    if (wave >= 2) {
+    const int f_base = (wave - CW) * FW;
+    if (wave >= CW) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -558,13 +566,12 @@ __global__ __launch_bounds__(kThreads, 2) void commit_chunks_kernel_bf16(CommitA
     // consumers: Z of rows f_base + 16 mt + l%16, kept (and stored) by lanes l < 16
     float zacc[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) zacc[mt] = (wave >= 2 && lg == 0) ? Zg[f_base + 16 * mt + li] : 0.f;
+    for (int mt = 0; mt < MT; ++mt) zacc[mt] = (wave >= CW && lg == 0) ? Zg[f_base + 16 * mt + li] : 0.f;
 
-    if (wave < 2) {
+    if (wave < CW) {
         // W^T into LDS: producer thread tid transposes 8x8 blocks (rows 8 bi..,
         // columns 8 bf..) of W (the consumers' loads are the state's)
-#pragma unroll
-        for (int blk = tid; blk < WBLK; blk += 128) {
+        for (int blk = tid; blk < WBLK; blk += NP) {
             const int bf = blk % (F / 8), bi = blk / (F / 8);
             uint4 wb[8];
 #pragma unroll
@@ -585,7 +592,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_chunks_kernel_bf16(CommitA
         // each requested two chunks ahead of its use.
         uint4 kA[KS], kB[KS];
         auto request = [&](int j, uint4 (&kin)[KS]) __attribute__((always_inline)) {
-            const int tk = j * kRows + 16 * wave + li;
+            const int tk = j * CT + 16 * wave + li;
             const T *kr = kg + (int64_t)(tk < nv ? tk : nv - 1) * D + 8 * lg;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) kin[ks] = *reinterpret_cast<const uint4 *>(kr + 32 * ks);
@@ -606,7 +613,7 @@ __global__ __launch_bounds__(kThreads, 2) void commit_chunks_kernel_bf16(CommitA
         // four tokens of one feature are one 16-byte write); tokens past the
         // chunk's valid ones get 0
         auto produce = [&](int j, const uint4 (&kin)[KS]) __attribute__((always_inline)) {
-            const int nrows = nv - j * kRows < kRows ? nv - j * kRows : kRows;
+            const int nrows = nv - j * CT < CT ? nv - j * CT : CT;
             floatx4 u[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) u[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -664,65 +671,78 @@ __global__ __launch_bounds__(kThreads, 2) void commit_chunks_kernel_bf16(CommitA
         }
     } else {
         // ------------------------------------------------------------ consumers
-        // V^T of chunk j into buffer j % 2: thread ct = tid - 128 takes tokens
-        // 4 (ct / 16) .. + 3, columns 8 (ct % 16) .. + 7; row rho of V^T holds
-        // the column that N-tile pair q gives lane l (32 q + 2 l and + 1).
-        // Two register sets, each requested two chunks ahead of its staging.
-        const int ct = tid - 128, cb = ct & 15, tq = ct >> 4;
+        // V^T of chunk j into buffer j % 2: consumer thread ct takes tokens
+        // 4 tq .. + 3 and columns 8 cb .. + 7 (eight lanes per 128-byte row
+        // segment); row rho of V^T holds the column that N-tile pair q gives
+        // lane l (32 q + 2 l and + 1).  Two register sets, each requested two
+        // chunks ahead of its staging.
+        const int ct = tid - NP;
+        const int tq = (ct & 7) + 8 * (ct >> 7), cb = (ct >> 3) & 15;
         uint4 vA[4], vB[4];
         auto request_v = [&](int j, uint4 (&vin)[4]) __attribute__((always_inline)) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int tv = j * kRows + 4 * tq + e;
+                const int tv = j * CT + 4 * tq + e;
                 vin[e] = *reinterpret_cast<const uint4 *>(vg + (int64_t)(tv < nv ? tv : nv - 1) * D + 8 * cb);
             }
         };
+        // The 8-byte writes go out 16 lanes at a time: lanes with odd cb take
+        // their columns in the order c ^ 4, two rows off their even
+        // neighbours', so that the 16 lanes of one write cover all 32 banks.
+        const bool odd = cb & 1;
+        const int rbase = 32 * (cb >> 2) + 4 * (cb & 3);
+        const int row_lo = rbase + (odd ? 2 : 0), row_hi = rbase - (odd ? 2 : 0);
         auto stage_v = [&](int j, const uint4 (&vin)[4]) __attribute__((always_inline)) {
-            const int nrows = nv - j * kRows < kRows ? nv - j * kRows : kRows;
-            T *vtb = vt_of(j & 1);
+            const int nrows = nv - j * CT < CT ? nv - j * CT : CT;
+            T *vtb = vt_of(j & 1) + 4 * tq;
             uint4 x[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const bool ok = 4 * tq + e < nrows;   // tokens past the valid ones: v = 0
-                x[e] = make_uint4(ok ? vin[e].x : 0u, ok ? vin[e].y : 0u, ok ? vin[e].z : 0u, ok ? vin[e].w : 0u);
+                const uint4 y = make_uint4(ok ? vin[e].x : 0u, ok ? vin[e].y : 0u, ok ? vin[e].z : 0u, ok ? vin[e].w : 0u);
+                x[e] = odd ? make_uint4(y.z, y.w, y.x, y.y) : y;   // word c/2 of column c ^ 4 at word c/2
             }
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                const int col = 8 * cb + c;
-                const int rho = (2 * (col >> 5) + (col & 1)) * 16 + ((col & 31) >> 1);
+                // column 8 cb + (c ^ 4 if odd): row 32 (cb/4) + 16 (c%2) + 4 (cb%4) + (c/2 ^ 2 if odd)
+                const int rho = (c < 4 ? row_lo : row_hi) + 16 * (c & 1) + (c >> 1);
                 const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
                 const uint32_t w0 = __builtin_amdgcn_perm(u4_word(x[1], c >> 1), u4_word(x[0], c >> 1), sel);
                 const uint32_t w1 = __builtin_amdgcn_perm(u4_word(x[3], c >> 1), u4_word(x[2], c >> 1), sel);
-                *reinterpret_cast<uint2 *>(vtb + rho * G::TP + 4 * tq) = make_uint2(w0, w1);
+                *reinterpret_cast<uint2 *>(vtb + rho * G::TP) = make_uint2(w0, w1);
             }
         };
-        // S += phi^T V for chunk j: A[f][t] = phi_f(k_t) (high + residual),
-        // B[t][col] = v_t[col]; the A values also give Z's token sums
+        // S += phi^T V for chunk j, K-step kk over tokens 32 kk ..: A[f][t] =
+        // phi_f(k_t) (high + residual), B[t][col] = v_t[col]; the A values
+        // also give Z's token sums
         auto consume = [&](int j) __attribute__((always_inline)) {
-            const float *phs = ph_of(j & 1) + (f_base + li) * G::PTLD + 8 * lg;
-            const T *vtb = vt_of(j & 1);
-            bf16x8 bv[NE];
 #pragma unroll
-            for (int nt = 0; nt < NE; ++nt) bv[nt] = *reinterpret_cast<const bf16x8 *>(vtb + (16 * nt + li) * G::TP + 8 * lg);
+            for (int kk = 0; kk < KC; ++kk) {
+                const float *phs = ph_of(j & 1) + (f_base + li) * G::PTLD + 32 * kk + 8 * lg;
+                const T *vtb = vt_of(j & 1) + 32 * kk + 8 * lg;
+                bf16x8 bv[NE];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const float4 x0 = *reinterpret_cast<const float4 *>(phs + 16 * mt * G::PTLD);
-                const float4 x1 = *reinterpret_cast<const float4 *>(phs + 16 * mt * G::PTLD + 4);
-                const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-                bf16x8 ah, al;
+                for (int nt = 0; nt < NE; ++nt) bv[nt] = *reinterpret_cast<const bf16x8 *>(vtb + (16 * nt + li) * G::TP);
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const __bf16 hx = (__bf16)xs[t];
-                    ah[t] = hx;
-                    al[t] = (__bf16)(xs[t] - (float)hx);
+                for (int mt = 0; mt < MT; ++mt) {
+                    const float4 x0 = *reinterpret_cast<const float4 *>(phs + 16 * mt * G::PTLD);
+                    const float4 x1 = *reinterpret_cast<const float4 *>(phs + 16 * mt * G::PTLD + 4);
+                    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                    bf16x8 ah, al;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const __bf16 hx = (__bf16)xs[t];
+                        ah[t] = hx;
+                        al[t] = (__bf16)(xs[t] - (float)hx);
+                    }
+#pragma unroll
+                    for (int nt = 0; nt < NE; ++nt) {
+                        acc[mt][nt] = mfma_bf16(ah, bv[nt], acc[mt][nt]);
+                        acc[mt][nt] = mfma_bf16(al, bv[nt], acc[mt][nt]);
+                    }
+                    // tokens 32 kk + 8 (l/16) .. + 7 of row f_base + 16 mt + l%16, then all 32
+                    zacc[mt] += xrow_sum(((xs[0] + xs[1]) + (xs[2] + xs[3])) + ((xs[4] + xs[5]) + (xs[6] + xs[7])));
                 }
-#pragma unroll
-                for (int nt = 0; nt < NE; ++nt) {
-                    acc[mt][nt] = mfma_bf16(ah, bv[nt], acc[mt][nt]);
-                    acc[mt][nt] = mfma_bf16(al, bv[nt], acc[mt][nt]);
-                }
-                // tokens 8 (l/16) .. + 7 of row f_base + 16 mt + l%16, then all 32
-                zacc[mt] += xrow_sum(((xs[0] + xs[1]) + (xs[2] + xs[3])) + ((xs[4] + xs[5]) + (xs[6] + xs[7])));
             }
         };
         request_v(0, vA);
@@ -983,8 +1003,13 @@ static hipError_t launch_commit_t(const CommitArgs &a, hipStream_t stream) {
                 return launch_kernel(commit_block_kernel_bf16<F>, grid, dim3(kThreads), a, stream);
             return launch_kernel(commit_kernel_bf16<D, F, false>, grid2, dim3(kThreads), a, stream);
         }
-        if constexpr (D == 128)   // several chunks: the pipelined form
-            return launch_kernel(commit_chunks_kernel_bf16<F>, grid2, dim3(kThreads), a, stream);
+        if constexpr (D == 128) {   // several chunks: the pipelined form
+            // at most one workgroup per CU: eight waves and 64-token chunks
+            const int64_t cus = device_cus();
+            if (cus > 0 && 2 * (int64_t)a.B * a.H <= cus)
+                return launch_kernel(commit_chunks_kernel_bf16<F, 4>, grid2, dim3(128 * 4), a, stream);
+            return launch_kernel(commit_chunks_kernel_bf16<F, 2>, grid2, dim3(kThreads), a, stream);
+        }
         return launch_kernel(commit_kernel_bf16<D, F, true>, grid2, dim3(kThreads), a, stream);
     } else {
         return launch_kernel(commit_kernel<T, D, F>, grid, dim3(kThreads), a, stream);

@@ -512,14 +512,19 @@ def test_commit_one_block_serving_shapes(B, T, F, Hkv):
     (12, 192, 128, 16, [0, 1, 32, 33, 64, 65, 96, 97, 128, 160, 191, 192]),
     (12, 192, 64, 4, [192, 191, 160, 128, 97, 96, 65, 64, 33, 32, 1, 0]),
     (4, 2048, 128, 16, [2048, 2047, 1025, 33]),
+    # 2 B H = 256 workgroups, at most one per CU on a 256-CU device: the
+    # eight-wave form with 64-token chunks
+    (8, 320, 128, 16, [0, 1, 64, 65, 128, 129, 257, 320]),
+    (8, 320, 64, 4, [320, 319, 192, 191, 127, 64, 33, 0]),
 ])
 def test_commit_multichunk_pipeline(B, T, F, Hkv, nvs):
-    """The pipelined bf16 commit (more than one 32-token chunk, d = 128): every
-    chunk count from 0 to T/32 over the requests, both parities of the
-    two-chunk loop and its one-chunk tail, a token count that is not a
-    multiple of 32, grouped key/value heads and a slot map into a larger
-    pool; every state against the oracle, untouched slots and n_valid = 0
-    pairs bitwise."""
+    """The pipelined bf16 commit (more than one 32-token chunk, d = 128), in
+    its four-wave (32-token chunks) and eight-wave (64-token chunks, grids of
+    at most one workgroup per CU) forms: every chunk count over the requests,
+    both parities of the two-chunk loop and its one-chunk tail, token counts
+    that are not a multiple of the chunk, grouped key/value heads and a slot
+    map into a larger pool; every state against the oracle, untouched slots
+    and n_valid = 0 pairs bitwise."""
     H, d = 16, 128
     dt = torch.bfloat16
     g = gen(8800 + B + T + F + Hkv)
