@@ -669,11 +669,13 @@ static hipError_t launch_step_t(const StepArgs &a, hipStream_t stream) {
     if constexpr (sizeof(T) == 2) {
         const int64_t items = (int64_t)a.B * a.H;
         if constexpr (D == 128) {
-            // fewer (request, head) pairs than CUs: split the output columns
-            // over two workgroups per pair (measured: 12.6 -> 12.0 us at
-            // B=8, H=16; slower once the pairs alone fill the CUs)
+            // at most half a workgroup per CU: split the output columns over
+            // two workgroups per pair.  Measured per launch from a HIP graph
+            // at H = 16: 9.8 -> 9.05 us at B = 8 and 8.65 -> 7.4 us at B = 1;
+            // between half and all of the CUs one workgroup per pair is
+            // faster (10.1-11.1 against 11.9-13.0 us at B = 9..15)
             const int64_t cus = device_cus();
-            if (cus > 0 && items < cus)
+            if (cus > 0 && 2 * items <= cus)
                 return launch_kernel(step_kernel_bf16<D, F, 2>, dim3((unsigned)(2 * items)), dim3(kThreads), a, stream);
         }
         return launch_kernel(step_kernel_bf16<D, F, 1>, dim3((unsigned)items), dim3(kThreads), a, stream);

@@ -52,12 +52,15 @@ struct FusedGeom {
     static_assert(KP - row_pad == 8, "four floats per A_hi row pad");
 };
 
-template <int D, int F>
+template <int D, int F, int NSPLIT>
 __global__ __launch_bounds__(kThreads, 2) void step_commit_kernel_bf16(StepCommitArgs a) {
     using T = uint16_t;
     using P = ProjGeom<T, D, F>;
     using G = FusedGeom<D, F>;
-    static_assert(D == 128, "four waves of 32 output columns");
+    // NSPLIT workgroups per (request, head), each owning D/NSPLIT value
+    // columns of the output and the state; each forms the whole prologue
+    static_assert(D == 128 && (NSPLIT == 1 || NSPLIT == 2), "four waves of 32 or 16 value columns");
+    constexpr int EPL = 2 / NSPLIT;   // columns per lane per N-tile
     constexpr int NCH = 2 * F / 32;   // 32-row chunks of the state, all held by every wave
     constexpr int RING = 2;           // chunks requested at entry (the rest after staging,
                                       // so that no wave has more than 63 loads in flight)
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(kThreads, 2) void step_commit_kernel_bf16(StepCommi
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int bh = (int)blockIdx.x;
+    const int bh = (int)blockIdx.x / NSPLIT, part = (int)blockIdx.x - bh * NSPLIT;
     const int b = bh / a.H, h = bh - b * a.H;
     const int L = a.L;
     int nv = a.n_valid ? a.n_valid[b] : L;
@@ -103,15 +106,19 @@ __global__ __launch_bounds__(kThreads, 2) void step_commit_kernel_bf16(StepCommi
     load_w<T, D, F>(Wg, wc);
     float4 zq = make_float4(0.f, 0.f, 0.f, 0.f);
     if (tid < ZQ) zq = reinterpret_cast<const float4 *>(Zg)[tid];
-    const int c0 = 32 * wave + 2 * li;
+    const int c0 = part * (D / NSPLIT) + (D / (4 * NSPLIT)) * wave + EPL * li;
     const int lofs = 8 * lg * D + c0;   // 32-bit element offsets from the uniform state base
-    float sreg[NCH][8][2];
+    float sreg[NCH][8][EPL];
     auto load_chunk = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const floatx2 v2 = __builtin_nontemporal_load(reinterpret_cast<const floatx2 *>(Sg + (lofs + (32 * c + t) * D)));
-            sreg[c][t][0] = v2[0];
-            sreg[c][t][1] = v2[1];
+            if constexpr (EPL == 2) {
+                const floatx2 v2 = __builtin_nontemporal_load(reinterpret_cast<const floatx2 *>(Sg + (lofs + (32 * c + t) * D)));
+                sreg[c][t][0] = v2[0];
+                sreg[c][t][1] = v2[1];
+            } else {
+                sreg[c][t][0] = __builtin_nontemporal_load(Sg + (lofs + (32 * c + t) * D));
+            }
         }
     };
 #pragma unroll
@@ -121,7 +128,8 @@ __global__ __launch_bounds__(kThreads, 2) void step_commit_kernel_bf16(StepCommi
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const int j = 8 * lg + t;
-        vw[t] = *reinterpret_cast<const uint32_t *>(vg + (j < L ? j : L - 1) * D + c0);
+        const T *p = vg + (j < L ? j : L - 1) * D + c0;
+        vw[t] = EPL == 2 ? *reinterpret_cast<const uint32_t *>(p) : (uint32_t)*p;
     }
     store_rows<T, D, F>(qc, qs);
     store_rows<T, D, F>(kc, ks);
@@ -294,28 +302,25 @@ __global__ __launch_bounds__(kThreads, 2) void step_commit_kernel_bf16(StepCommi
     __syncthreads();
 
     // 4. the stream: step contraction, then S + phi(K)^T V stored in place
-    floatx4 accS[2][2], accV[2][2];
+    floatx4 accS[2][EPL], accV[2][EPL];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int e = 0; e < 2; ++e) accS[t][e] = accV[t][e] = floatx4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 bv[2];
-    {
-        uint32_t p0[4], p1[4];
+        for (int e = 0; e < EPL; ++e) accS[t][e] = accV[t][e] = floatx4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 bv[EPL];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            p0[j] = __builtin_amdgcn_perm(vw[2 * j + 1], vw[2 * j], 0x05040100u);
-            p1[j] = __builtin_amdgcn_perm(vw[2 * j + 1], vw[2 * j], 0x07060302u);
-        }
-        bv[0] = __builtin_bit_cast(bf16x8, make_uint4(p0[0], p0[1], p0[2], p0[3]));
-        bv[1] = __builtin_bit_cast(bf16x8, make_uint4(p1[0], p1[1], p1[2], p1[3]));
+    for (int e = 0; e < EPL; ++e) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pk[j] = __builtin_amdgcn_perm(vw[2 * j + 1], vw[2 * j], e ? 0x07060302u : 0x05040100u);
+        bv[e] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
     }
     const bool commit = nv > 0;   // nothing to fold: the state is left untouched
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-        bf16x8 bh_[2], bl_[2];
+        bf16x8 bh_[EPL], bl_[EPL];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
+        for (int e = 0; e < EPL; ++e) {
             uint32_t hw[4], lw[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) split_pk_bf16(sreg[c][2 * j][e], sreg[c][2 * j + 1][e], hw[j], lw[j]);
@@ -328,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 2) void step_commit_kernel_bf16(StepCommi
             const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(Ahi + (16 * mt + li) * G::KP + k0);
             const bf16x8 al = *reinterpret_cast<const bf16x8 *>(Alo + (16 * mt + li) * G::KP + k0);
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
+            for (int e = 0; e < EPL; ++e) {
                 accS[mt][e] = mfma_bf16(ah, bh_[e], accS[mt][e]);
                 accS[mt][e] = mfma_bf16(ah, bl_[e], accS[mt][e]);
                 accS[mt][e] = mfma_bf16(al, bh_[e], accS[mt][e]);
@@ -342,16 +347,21 @@ __global__ __launch_bounds__(kThreads, 2) void step_commit_kernel_bf16(StepCommi
             for (int mt = 0; mt < 2; ++mt) {
                 const bf16x8 kh = *reinterpret_cast<const bf16x8 *>(Khi + (frow + 4 * mt) * G::KT + 8 * lg);
                 const bf16x8 kl = *reinterpret_cast<const bf16x8 *>(Klo + (frow + 4 * mt) * G::KT + 8 * lg);
-                floatx4 ds[2];
+                floatx4 ds[EPL];
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
+                for (int e = 0; e < EPL; ++e) {
                     ds[e] = mfma_bf16(kh, bv[e], floatx4{0.f, 0.f, 0.f, 0.f});
                     ds[e] = mfma_bf16(kl, bv[e], ds[e]);
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const floatx2 o2 = {sreg[c][4 * mt + r][0] + ds[0][r], sreg[c][4 * mt + r][1] + ds[1][r]};
-                    __builtin_nontemporal_store(o2, reinterpret_cast<floatx2 *>(Sg + (lofs + (32 * c + 4 * mt + r) * D)));
+                    float *o = Sg + (lofs + (32 * c + 4 * mt + r) * D);
+                    if constexpr (EPL == 2) {
+                        const floatx2 o2 = {sreg[c][4 * mt + r][0] + ds[0][r], sreg[c][4 * mt + r][1] + ds[1][r]};
+                        __builtin_nontemporal_store(o2, reinterpret_cast<floatx2 *>(o));
+                    } else {
+                        __builtin_nontemporal_store(sreg[c][4 * mt + r][0] + ds[0][r], o);
+                    }
                 }
             }
         }
@@ -361,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 2) void step_commit_kernel_bf16(StepCommi
         const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(Ahi + (16 * mt + li) * G::KP + 8 * lg);
         const bf16x8 al = *reinterpret_cast<const bf16x8 *>(Alo + (16 * mt + li) * G::KP + 8 * lg);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
+        for (int e = 0; e < EPL; ++e) {
             accV[mt][e] = mfma_bf16(ah, bv[e], accV[mt][e]);
             accV[mt][e] = mfma_bf16(al, bv[e], accV[mt][e]);
         }
@@ -383,22 +393,35 @@ __global__ __launch_bounds__(kThreads, 2) void step_commit_kernel_bf16(StepCommi
                 const float sv = fast_exp2(g2 - cc);
                 const float ss = ld > 0.f ? fast_exp2(-cc) : 0.f;
                 const float inv = __builtin_amdgcn_rcpf(sv * as + ss * ld);
-                const floatx2 v2 = {(sv * accV[mt][0][r] + ss * accS[mt][0][r]) * inv,
-                                    (sv * accV[mt][1][r] + ss * accS[mt][1][r]) * inv};
-                __builtin_nontemporal_store(v2, reinterpret_cast<floatx2 *>(og + (int64_t)i * D + c0));
+                float *o = og + (int64_t)i * D + c0;
+                if constexpr (EPL == 2) {
+                    const floatx2 v2 = {(sv * accV[mt][0][r] + ss * accS[mt][0][r]) * inv,
+                                        (sv * accV[mt][1][r] + ss * accS[mt][1][r]) * inv};
+                    __builtin_nontemporal_store(v2, reinterpret_cast<floatx2 *>(o));
+                } else {
+                    __builtin_nontemporal_store((sv * accV[mt][0][r] + ss * accS[mt][0][r]) * inv, o);
+                }
             }
         }
     }
-    // 6. Z += sum_t phi(k_t)
-    if (commit && tid < 2 * F) __builtin_nontemporal_store(zs[tid] + zk[tid] + zk[2 * F + tid], Zg + tid);
+    // 6. Z += sum_t phi(k_t), by the first workgroup of the pair
+    if (commit && part == 0 && tid < 2 * F) __builtin_nontemporal_store(zs[tid] + zk[tid] + zk[2 * F + tid], Zg + tid);
 }
 
 hipError_t launch_step_commit(const StepCommitArgs &a, bool bf16, int d, int F, hipStream_t stream) {
     if (bf16 && d == 128) {
+        // at most half a workgroup per CU: split the value columns over two
+        // workgroups per pair (13.7 -> 12.8 us at B = 8, H = 16; slower at
+        // B = 12 and 16, 14.4 -> 17.6 and 16.6 -> 18.6 us)
+        const int64_t items = (int64_t)a.B * a.H, cus = device_cus();
+        const bool split = cus > 0 && 2 * items <= cus;
+        const dim3 grid((unsigned)(split ? 2 * items : items));
         if (F == 128)
-            return launch_kernel(step_commit_kernel_bf16<128, 128>, dim3((unsigned)(a.B * a.H)), dim3(kThreads), a, stream);
+            return split ? launch_kernel(step_commit_kernel_bf16<128, 128, 2>, grid, dim3(kThreads), a, stream)
+                         : launch_kernel(step_commit_kernel_bf16<128, 128, 1>, grid, dim3(kThreads), a, stream);
         if (F == 64)
-            return launch_kernel(step_commit_kernel_bf16<128, 64>, dim3((unsigned)(a.B * a.H)), dim3(kThreads), a, stream);
+            return split ? launch_kernel(step_commit_kernel_bf16<128, 64, 2>, grid, dim3(kThreads), a, stream)
+                         : launch_kernel(step_commit_kernel_bf16<128, 64, 1>, grid, dim3(kThreads), a, stream);
     }
     // other shapes: the step on the current state, then the commit
     const StepArgs s{a.q, a.k, a.v, a.W, a.gate, a.S, a.Z, a.slot, a.out, a.B, a.H, a.L, a.G};
