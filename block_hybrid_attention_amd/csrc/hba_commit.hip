@@ -7,9 +7,10 @@
 // The commit is a read-modify-write of the fp32 state (2 x 128 KB at
 // F = d = 128) plus a small contraction Phi^T V (K = tokens).  Four kernels:
 //   * commit_kernel: fp32 inputs (described here);
-//   * commit_kernel_bf16: bf16 inputs, one workgroup per state half (d = 64);
+//   * commit_kernel_bf16: bf16 inputs, one workgroup per state half (d = 64;
+//     d = 128 for one block when the pairs fill at most half of the CUs);
 //   * commit_block_kernel_bf16: bf16, d = 128, one block of at most 32
-//     tokens, one workgroup per (request, head);
+//     tokens, one workgroup per (request, head), above half of the CUs;
 //   * commit_chunks_kernel_bf16: bf16, d = 128, several chunks of 32 or 64
 //     tokens, pipelined.
 // fp32 inputs: one workgroup (4 waves) per (request, head).
@@ -999,8 +1000,15 @@ static hipError_t launch_commit_t(const CommitArgs &a, hipStream_t stream) {
     if constexpr (sizeof(T) == 2) {
         const dim3 grid2((unsigned)(2 * a.B * a.H));   // one workgroup per state half
         if (a.T <= kRows) {   // one block
-            if constexpr (D == 128)
+            if constexpr (D == 128) {
+                // at most half a workgroup per CU: one workgroup per state
+                // half (9.1-9.2 against 11.4 us at B = 8, H = 16; slower
+                // from B = 10 on, 12.5 against 11.5 us)
+                const int64_t cus = device_cus();
+                if (cus > 0 && 2 * (int64_t)a.B * a.H <= cus)
+                    return launch_kernel(commit_kernel_bf16<D, F, false>, grid2, dim3(kThreads), a, stream);
                 return launch_kernel(commit_block_kernel_bf16<F>, grid, dim3(kThreads), a, stream);
+            }
             return launch_kernel(commit_kernel_bf16<D, F, false>, grid2, dim3(kThreads), a, stream);
         }
         if constexpr (D == 128) {   // several chunks: the pipelined form
