@@ -506,7 +506,7 @@ __global__ __launch_bounds__(128 * CW, CW == 2 ? 2 : 1) void commit_chunks_kerne
     constexpr int CT = G::CT;
     constexpr int NT = F / 16;          // feature tiles of this half
     constexpr int KS = D / 32;          // K-steps of the projection
-    constexpr int NE = D / 16;          // N-tiles of the state, paired as in commit_kernel_bf16
+    constexpr int NE = D / 16;          // N-tiles of the state: tile nt, lane l holds column 64 (nt/4) + 4 (l%16) + nt%4
     constexpr int FW = F / CW;          // state rows per consumer wave
     constexpr int MT = FW / 16;
     constexpr int KC = CT / 32;         // K-steps of the contraction per chunk
@@ -555,12 +555,13 @@ __global__ __launch_bounds__(128 * CW, CW == 2 ? 2 : 1) void commit_chunks_kerne
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float *p = Sg + (int64_t)(f_base + 16 * mt + 4 * lg + r) * D + 2 * li;
+                // four consecutive columns per lane: 256-byte row segments per 16 lanes
+                const float *p = Sg + (int64_t)(f_base + 16 * mt + 4 * lg + r) * D + 4 * li;
 #pragma unroll
-                for (int q = 0; q < NE / 2; ++q) {
-                    const floatx2 t = __builtin_nontemporal_load(reinterpret_cast<const floatx2 *>(p + 32 * q));
-                    acc[mt][2 * q + 0][r] = t[0];
-                    acc[mt][2 * q + 1][r] = t[1];
+                for (int q = 0; q < NE / 4; ++q) {
+                    const floatx4 t = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p + 64 * q));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[mt][4 * q + e][r] = t[e];
                 }
             }
     }
@@ -674,9 +675,9 @@ __global__ __launch_bounds__(128 * CW, CW == 2 ? 2 : 1) void commit_chunks_kerne
         // ------------------------------------------------------------ consumers
         // V^T of chunk j into buffer j % 2: consumer thread ct takes tokens
         // 4 tq .. + 3 and columns 8 cb .. + 7 (eight lanes per 128-byte row
-        // segment); row rho of V^T holds the column that N-tile pair q gives
-        // lane l (32 q + 2 l and + 1).  Two register sets, each requested two
-        // chunks ahead of its staging.
+        // segment); row rho = 16 nt + l of V^T holds the column that N-tile
+        // nt gives lane l, 64 (nt/4) + 4 l + nt%4.  Two register sets, each
+        // requested two chunks ahead of its staging.
         const int ct = tid - NP;
         const int tq = (ct & 7) + 8 * (ct >> 7), cb = (ct >> 3) & 15;
         uint4 vA[4], vB[4];
@@ -687,12 +688,11 @@ __global__ __launch_bounds__(128 * CW, CW == 2 ? 2 : 1) void commit_chunks_kerne
                 vin[e] = *reinterpret_cast<const uint4 *>(vg + (int64_t)(tv < nv ? tv : nv - 1) * D + 8 * cb);
             }
         };
-        // The 8-byte writes go out 16 lanes at a time: lanes with odd cb take
-        // their columns in the order c ^ 4, two rows off their even
-        // neighbours', so that the 16 lanes of one write cover all 32 banks.
-        const bool odd = cb & 1;
-        const int rbase = 32 * (cb >> 2) + 4 * (cb & 3);
-        const int row_lo = rbase + (odd ? 2 : 0), row_hi = rbase - (odd ? 2 : 0);
+        // Column 8 cb + c sits in row 64 (cb/8) + 16 (c%4) + 2 (cb%8) + c/4.
+        // The 8-byte writes go out 16 lanes at a time (eight token quads of
+        // two neighbouring column blocks); the two blocks' rows are 2 apart,
+        // 16 banks at these row strides, so one write covers all 32 banks.
+        const int rbase = 64 * (cb >> 3) + 2 * (cb & 7);
         auto stage_v = [&](int j, const uint4 (&vin)[4]) __attribute__((always_inline)) {
             const int nrows = nv - j * CT < CT ? nv - j * CT : CT;
             T *vtb = vt_of(j & 1) + 4 * tq;
@@ -700,13 +700,11 @@ __global__ __launch_bounds__(128 * CW, CW == 2 ? 2 : 1) void commit_chunks_kerne
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const bool ok = 4 * tq + e < nrows;   // tokens past the valid ones: v = 0
-                const uint4 y = make_uint4(ok ? vin[e].x : 0u, ok ? vin[e].y : 0u, ok ? vin[e].z : 0u, ok ? vin[e].w : 0u);
-                x[e] = odd ? make_uint4(y.z, y.w, y.x, y.y) : y;   // word c/2 of column c ^ 4 at word c/2
+                x[e] = make_uint4(ok ? vin[e].x : 0u, ok ? vin[e].y : 0u, ok ? vin[e].z : 0u, ok ? vin[e].w : 0u);
             }
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                // column 8 cb + (c ^ 4 if odd): row 32 (cb/4) + 16 (c%2) + 4 (cb%4) + (c/2 ^ 2 if odd)
-                const int rho = (c < 4 ? row_lo : row_hi) + 16 * (c & 1) + (c >> 1);
+                const int rho = rbase + 16 * (c & 3) + (c >> 2);
                 const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
                 const uint32_t w0 = __builtin_amdgcn_perm(u4_word(x[1], c >> 1), u4_word(x[0], c >> 1), sel);
                 const uint32_t w1 = __builtin_amdgcn_perm(u4_word(x[3], c >> 1), u4_word(x[2], c >> 1), sel);
@@ -776,11 +774,12 @@ __global__ __launch_bounds__(128 * CW, CW == 2 ? 2 : 1) void commit_chunks_kerne
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float *p = Sg + (int64_t)(f_base + 16 * mt + 4 * lg + r) * D + 2 * li;
+                float *p = Sg + (int64_t)(f_base + 16 * mt + 4 * lg + r) * D + 4 * li;
 #pragma unroll
-                for (int q = 0; q < NE / 2; ++q)
-                    __builtin_nontemporal_store(floatx2{acc[mt][2 * q + 0][r], acc[mt][2 * q + 1][r]},
-                                                reinterpret_cast<floatx2 *>(p + 32 * q));
+                for (int q = 0; q < NE / 4; ++q)
+                    __builtin_nontemporal_store(floatx4{acc[mt][4 * q][r], acc[mt][4 * q + 1][r], acc[mt][4 * q + 2][r],
+                                                        acc[mt][4 * q + 3][r]},
+                                                reinterpret_cast<floatx4 *>(p + 64 * q));
             }
         if (lg == 0) {
 #pragma unroll
