@@ -4,6 +4,7 @@
     python bench.py --comparator     # hybrid step vs full softmax over P-token caches
     python bench.py --decode-loop    # B=32 decode loop: 8 steps + 1 commit per block
     python bench.py --commit-sweep   # whole-prefix commits (pipelined kernel), B=8..128
+    python bench.py --small-batch    # step, commit, fused step + commit at B=1..32 (HIP graphs)
 
 Workload (one hybrid layer): 128 requests, 16 heads, head_dim 128, F = 128
 (phi dim 256), active block 32 tokens, bf16 q/k/v/W ~ N(0,1) / N(0,1/d), fp32
@@ -284,6 +285,46 @@ def commit_sweep(args, torch, hba, wl, dev):
     return rows
 
 
+def small_batch(args, torch, hba, wl, dev):
+    """The decode-path calls at small batches (bf16, H=16, d=F=128, L=32):
+    hba_step, the one-block hba_commit and hba_step_commit, each replayed
+    from a HIP graph (a decode loop's launches; one launch takes a few
+    microseconds, so the host is kept out of the timing) over rotating state
+    sets.  Below half a workgroup per CU the library splits each (request,
+    head) over two workgroups; these batch sizes show both sides of that."""
+    H, L, d, F = 16, 32, 128, 128
+    batches = [int(x) for x in (args.batch if args.batch != "128" else "1,4,8,12,16,32").split(",")]
+    stream = torch.cuda.current_stream()
+    rows = []
+    for B in batches:
+        g = wl.generator(57 + B, dev)
+        W = wl.feature_weights(H, d, F, torch.bfloat16, g, dev)
+        q, k, v = wl.block_qkv(B, H, L, d, torch.bfloat16, g, dev)
+        per_set = B * H * (2 * F * d + 2 * F) * 4
+        nsets = max(2, min(16, -(-600_000_000 // per_set)))
+        sets = [(wl.normal((B, H, 2 * F, d), 0.01, torch.float32, g, dev),
+                 torch.rand((B, H, 2 * F), generator=g, device=dev) * 20 + 1) for _ in range(nsets)]
+        out = torch.empty((B, H, L, d), device=dev)
+        it = [0]
+
+        def nxt():
+            S, Z = sets[it[0] % nsets]
+            it[0] += 1
+            return S, Z
+
+        calls = {"step": lambda: hba.step(q, k, v, W, *nxt(), out=out),
+                 "commit": lambda: hba.commit(k, v, W, *nxt()),
+                 "step_commit": lambda: hba.step_commit(q, k, v, W, *nxt(), out=out)}
+        row = {"batch": B, "items": B * H}
+        for name, fn in calls.items():
+            row[name + "_us"] = _time_graph(torch, fn, nsets, max(2, args.steps // nsets), stream) * 1e3
+        rows.append(row)
+        print(json.dumps({"mode": "small_batch", **row}), flush=True)
+        del sets
+        torch.cuda.empty_cache()
+    return rows
+
+
 def batch_sweep(args, torch, hba, wl, dev):
     """hba_step (bf16, H=16, d=F=128, L=32) over batch sizes, with enough
     rotating state sets (> 600 MB) that the 256 MB Infinity Cache holds none
@@ -459,6 +500,9 @@ def main():
                     help="time hba_step over batch sizes (--batch, default 16..192) and fit fixed + marginal cost")
     ap.add_argument("--commit-sweep", action="store_true",
                     help="hba_commit of whole prefixes (8 x 2048 .. 128 x 2048 tokens)")
+    ap.add_argument("--small-batch", action="store_true",
+                    help="hba_step, one-block hba_commit and hba_step_commit at small batches "
+                         "(--batch, default 1..32), each replayed from a HIP graph")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB read + 1 GiB write elementwise kernel (torch.neg) "
                          "10 times, to calibrate HBM byte counters")
@@ -496,6 +540,8 @@ def main():
         return commit_sweep(args, torch, hba, wl, dev)
     if args.batch_sweep:
         return batch_sweep(args, torch, hba, wl, dev)
+    if args.small_batch:
+        return small_batch(args, torch, hba, wl, dev)
     c = wl.serving_b128()
     B, H, L, d, F = c.batch, c.heads, c.block, c.head_dim, c.feat
     plen = torch.tensor(c.prefix, dtype=torch.int32)
