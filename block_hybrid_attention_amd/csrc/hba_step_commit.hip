@@ -19,13 +19,18 @@
 //     holds four consecutive tokens of one feature): phi(K)^T goes to LDS as
 //     a bf16 high part and residual in [feature][token] order, and the
 //     per-feature token sums for Z are taken in registers.
-//   * Wave w owns output columns 32 w .. +31 (two per lane) of all 2F state
-//     rows and holds its whole column slice in registers, requested before
-//     the prologue.  Per 32-row chunk it runs the step's contraction and then
-//     dS = phi(K)^T V on bf16 MFMA, whose B operand is the block values it
-//     already holds for the step; the A rows are taken in the order that
+//   * Wave w owns the F state rows of feature half w / 2 and the value
+//     columns of column block w mod 2 (64 columns, four per lane, or 32 with
+//     two workgroups per pair), and holds that slice in registers, requested
+//     before the prologue: every state access is a 16-byte (8-byte) access,
+//     a 256-byte (128-byte) row segment per 16 lanes.  Per 32-row chunk it
+//     runs its part of the step's contraction (this half's features) and
+//     then dS = phi(K)^T V on bf16 MFMA, whose B operand is the block values
+//     it already holds for the step; the A rows are taken in the order that
 //     makes dS land in exactly the lanes and rows that hold the streamed
 //     chunk, so S + dS is stored in place at once.
+//   * The two halves' step partials of a column block meet in LDS; the wave
+//     of the first half adds the block-softmax part, merges and stores.
 // Other dtypes and shapes run the step kernel, then the commit kernel.
 #include "hba_device.h"
 #include "hba_internal.h"
@@ -59,11 +64,11 @@ __global__ __launch_bounds__(kThreads, 2) void step_commit_kernel_bf16(StepCommi
     using G = FusedGeom<D, F>;
     // NSPLIT workgroups per (request, head), each owning D/NSPLIT value
     // columns of the output and the state; each forms the whole prologue
-    static_assert(D == 128 && (NSPLIT == 1 || NSPLIT == 2), "four waves of 32 or 16 value columns");
-    constexpr int EPL = 2 / NSPLIT;   // columns per lane per N-tile
-    constexpr int NCH = 2 * F / 32;   // 32-row chunks of the state, all held by every wave
-    constexpr int RING = 2;           // chunks requested at entry (the rest after staging,
-                                      // so that no wave has more than 63 loads in flight)
+    static_assert(D == 128 && (NSPLIT == 1 || NSPLIT == 2), "two column blocks of 64 or 32 value columns");
+    constexpr int EPL = 4 / NSPLIT;   // columns per lane (N-tiles of the state contraction)
+    constexpr int CB = 16 * EPL;      // columns per wave
+    constexpr int NCH = F / 32;       // 32-row chunks of this wave's feature half
+    constexpr int RING = 1;           // chunks requested at entry (the rest after staging)
     constexpr int NT = F / 16;
     constexpr int KS = D / 32;
     constexpr int ZQ = 2 * F / 4;
@@ -106,30 +111,41 @@ __global__ __launch_bounds__(kThreads, 2) void step_commit_kernel_bf16(StepCommi
     load_w<T, D, F>(Wg, wc);
     float4 zq = make_float4(0.f, 0.f, 0.f, 0.f);
     if (tid < ZQ) zq = reinterpret_cast<const float4 *>(Zg)[tid];
-    const int c0 = part * (D / NSPLIT) + (D / (4 * NSPLIT)) * wave + EPL * li;
-    const int lofs = 8 * lg * D + c0;   // 32-bit element offsets from the uniform state base
+    const int sh = wave >> 1;   // feature half of this wave's state rows
+    const int c0 = part * (D / NSPLIT) + CB * (wave & 1) + EPL * li;   // its columns c0 .. c0 + EPL - 1
+    // chunk c holds rows sh F + 32 c + 8 lg + t (t < 8); 32-bit element
+    // offsets from the uniform state base
+    const int lofs = (sh * F + 8 * lg) * D + c0;
     float sreg[NCH][8][EPL];
     auto load_chunk = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            if constexpr (EPL == 2) {
+            if constexpr (EPL == 4) {
+                const floatx4 v4 = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(Sg + (lofs + (32 * c + t) * D)));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sreg[c][t][e] = v4[e];
+            } else {
                 const floatx2 v2 = __builtin_nontemporal_load(reinterpret_cast<const floatx2 *>(Sg + (lofs + (32 * c + t) * D)));
                 sreg[c][t][0] = v2[0];
                 sreg[c][t][1] = v2[1];
-            } else {
-                sreg[c][t][0] = __builtin_nontemporal_load(Sg + (lofs + (32 * c + t) * D));
             }
         }
     };
 #pragma unroll
     for (int c = 0; c < RING; ++c) load_chunk(c);
     const float lw2 = a.gate ? __log2f(a.gate[h]) : 0.f;   // log2 w
-    uint32_t vw[8];
+    uint32_t vw[8][EPL / 2];   // tokens 8 lg + t, columns c0 .. (two per word)
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const int j = 8 * lg + t;
         const T *p = vg + (j < L ? j : L - 1) * D + c0;
-        vw[t] = EPL == 2 ? *reinterpret_cast<const uint32_t *>(p) : (uint32_t)*p;
+        if constexpr (EPL == 4) {
+            const uint2 w2 = *reinterpret_cast<const uint2 *>(p);
+            vw[t][0] = w2.x;
+            vw[t][1] = w2.y;
+        } else {
+            vw[t][0] = *reinterpret_cast<const uint32_t *>(p);
+        }
     }
     store_rows<T, D, F>(qc, qs);
     store_rows<T, D, F>(kc, ks);
@@ -301,48 +317,52 @@ __global__ __launch_bounds__(kThreads, 2) void step_commit_kernel_bf16(StepCommi
     }
     __syncthreads();
 
-    // 4. the stream: step contraction, then S + phi(K)^T V stored in place
-    floatx4 accS[2][EPL], accV[2][EPL];
+    // 4. the stream: this half's step contraction, then S + phi(K)^T V
+    //    stored in place
+    floatx4 accS[2][EPL];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) accS[t][e] = accV[t][e] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < EPL; ++e) accS[t][e] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // N-tile e: lane l%16 supplies column c0 + e of tokens 8(l/16) ..
     bf16x8 bv[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
         uint32_t pk[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pk[j] = __builtin_amdgcn_perm(vw[2 * j + 1], vw[2 * j], e ? 0x07060302u : 0x05040100u);
+        for (int j = 0; j < 4; ++j)
+            pk[j] = __builtin_amdgcn_perm(vw[2 * j + 1][e >> 1], vw[2 * j][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
         bv[e] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
     }
     const bool commit = nv > 0;   // nothing to fold: the state is left untouched
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-        bf16x8 bh_[EPL], bl_[EPL];
+        const int k0 = kRows + sh * F + 32 * c + 8 * lg;
+        bf16x8 ah[2], al[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            ah[mt] = *reinterpret_cast<const bf16x8 *>(Ahi + (16 * mt + li) * G::KP + k0);
+            al[mt] = *reinterpret_cast<const bf16x8 *>(Alo + (16 * mt + li) * G::KP + k0);
+        }
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
+            // column c0 + e of the chunk's rows 8 lg + t, split
             uint32_t hw[4], lw[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) split_pk_bf16(sreg[c][2 * j][e], sreg[c][2 * j + 1][e], hw[j], lw[j]);
-            bh_[e] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-            bl_[e] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-        }
-        const int k0 = kRows + 32 * c + 8 * lg;
+            const bf16x8 bh_ = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+            const bf16x8 bl_ = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(Ahi + (16 * mt + li) * G::KP + k0);
-            const bf16x8 al = *reinterpret_cast<const bf16x8 *>(Alo + (16 * mt + li) * G::KP + k0);
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                accS[mt][e] = mfma_bf16(ah, bh_[e], accS[mt][e]);
-                accS[mt][e] = mfma_bf16(ah, bl_[e], accS[mt][e]);
-                accS[mt][e] = mfma_bf16(al, bh_[e], accS[mt][e]);
+            for (int mt = 0; mt < 2; ++mt) {
+                accS[mt][e] = mfma_bf16(ah[mt], bh_, accS[mt][e]);
+                accS[mt][e] = mfma_bf16(ah[mt], bl_, accS[mt][e]);
+                accS[mt][e] = mfma_bf16(al[mt], bh_, accS[mt][e]);
             }
         }
         if (commit) {
             // dS tile mt, row 4(l/16) + r = chunk row 8(l/16) + 4 mt + r: the A
-            // operand row of lane l%16 = 4 g + r' is state row 32c + 8g + 4mt + r'
-            const int frow = 32 * c + 8 * (li >> 2) + (li & 3);
+            // operand row of lane l%16 = 4 g + r' is state row sh F + 32c + 8g + 4mt + r'
+            const int frow = sh * F + 32 * c + 8 * (li >> 2) + (li & 3);
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 const bf16x8 kh = *reinterpret_cast<const bf16x8 *>(Khi + (frow + 4 * mt) * G::KT + 8 * lg);
@@ -356,50 +376,86 @@ __global__ __launch_bounds__(kThreads, 2) void step_commit_kernel_bf16(StepCommi
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     float *o = Sg + (lofs + (32 * c + 4 * mt + r) * D);
-                    if constexpr (EPL == 2) {
+                    if constexpr (EPL == 4) {
+                        const floatx4 o4 = {sreg[c][4 * mt + r][0] + ds[0][r], sreg[c][4 * mt + r][1] + ds[1][r],
+                                            sreg[c][4 * mt + r][2] + ds[2][r], sreg[c][4 * mt + r][3] + ds[3][r]};
+                        __builtin_nontemporal_store(o4, reinterpret_cast<floatx4 *>(o));
+                    } else {
                         const floatx2 o2 = {sreg[c][4 * mt + r][0] + ds[0][r], sreg[c][4 * mt + r][1] + ds[1][r]};
                         __builtin_nontemporal_store(o2, reinterpret_cast<floatx2 *>(o));
-                    } else {
-                        __builtin_nontemporal_store(sreg[c][4 * mt + r][0] + ds[0][r], o);
                     }
                 }
             }
         }
     }
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(Ahi + (16 * mt + li) * G::KP + 8 * lg);
-        const bf16x8 al = *reinterpret_cast<const bf16x8 *>(Alo + (16 * mt + li) * G::KP + 8 * lg);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            accV[mt][e] = mfma_bf16(ah, bv[e], accV[mt][e]);
-            accV[mt][e] = mfma_bf16(al, bv[e], accV[mt][e]);
-        }
-    }
 
-    // 5. merge with one shift per query, out = (sv accV + ss accS) / (sv a + ss ld)
-    float *og = a.out + (int64_t)bh * L * D;
+    // 5. the second half's partials meet the first half's in LDS (over
+    //    phi(K)^T, dead after the stream); the first half's wave adds the
+    //    block-softmax part, merges with one shift per query and stores:
+    //    out = (sv accV + ss accS) / (sv a + ss ld)
+    constexpr int RLD = CB + 4;   // partial tile row stride (floats)
+    static_assert(2 * kRows * RLD * 4 <= G::kt_bytes, "partials fit the phi(K)^T area");
+    float *red = reinterpret_cast<float *>(smem + G::kt_off) + (wave & 1) * kRows * RLD;
+    __syncthreads();   // every wave is done with phi(K)^T
+    if (sh == 1) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * mt + 4 * lg + r;
-            if (i < L) {
-                const float4 rv = *reinterpret_cast<const float4 *>(rowv(i));
-                const float ld = rv.x + rv.y, g2 = rv.z + lw2, as = rv.w;
-                float cc = g2;
-                if (ld > 0.f) cc = fmaxf(cc, __log2f(ld));
-                cc = fmaxf(cc, -120.f);
-                const float sv = fast_exp2(g2 - cc);
-                const float ss = ld > 0.f ? fast_exp2(-cc) : 0.f;
-                const float inv = __builtin_amdgcn_rcpf(sv * as + ss * ld);
-                float *o = og + (int64_t)i * D + c0;
-                if constexpr (EPL == 2) {
-                    const floatx2 v2 = {(sv * accV[mt][0][r] + ss * accS[mt][0][r]) * inv,
-                                        (sv * accV[mt][1][r] + ss * accS[mt][1][r]) * inv};
-                    __builtin_nontemporal_store(v2, reinterpret_cast<floatx2 *>(o));
+            for (int r = 0; r < 4; ++r) {
+                float *rp = red + (16 * mt + 4 * lg + r) * RLD + EPL * li;
+                if constexpr (EPL == 4)
+                    *reinterpret_cast<floatx4 *>(rp) = floatx4{accS[mt][0][r], accS[mt][1][r], accS[mt][2][r], accS[mt][3][r]};
+                else
+                    *reinterpret_cast<floatx2 *>(rp) = floatx2{accS[mt][0][r], accS[mt][1][r]};
+            }
+    }
+    __syncthreads();
+    if (sh == 0) {
+        floatx4 accV[2][EPL];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(Ahi + (16 * mt + li) * G::KP + 8 * lg);
+            const bf16x8 al = *reinterpret_cast<const bf16x8 *>(Alo + (16 * mt + li) * G::KP + 8 * lg);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                accV[mt][e] = mfma_bf16(ah, bv[e], floatx4{0.f, 0.f, 0.f, 0.f});
+                accV[mt][e] = mfma_bf16(al, bv[e], accV[mt][e]);
+            }
+        }
+        float *og = a.out + (int64_t)bh * L * D;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * mt + 4 * lg + r;
+                const float *rp = red + i * RLD + EPL * li;
+                float pv[EPL];
+                if constexpr (EPL == 4) {
+                    const floatx4 p4 = *reinterpret_cast<const floatx4 *>(rp);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pv[e] = p4[e];
                 } else {
-                    __builtin_nontemporal_store((sv * accV[mt][0][r] + ss * accS[mt][0][r]) * inv, o);
+                    const floatx2 p2 = *reinterpret_cast<const floatx2 *>(rp);
+                    pv[0] = p2[0];
+                    pv[1] = p2[1];
+                }
+                if (i < L) {
+                    const float4 rv = *reinterpret_cast<const float4 *>(rowv(i));
+                    const float ld = rv.x + rv.y, g2 = rv.z + lw2, as = rv.w;
+                    float cc = g2;
+                    if (ld > 0.f) cc = fmaxf(cc, __log2f(ld));
+                    cc = fmaxf(cc, -120.f);
+                    const float sv = fast_exp2(g2 - cc);
+                    const float ss = ld > 0.f ? fast_exp2(-cc) : 0.f;
+                    const float inv = __builtin_amdgcn_rcpf(sv * as + ss * ld);
+                    float ov[EPL];
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) ov[e] = (sv * accV[mt][e][r] + ss * (accS[mt][e][r] + pv[e])) * inv;
+                    float *o = og + (int64_t)i * D + c0;
+                    if constexpr (EPL == 4)
+                        __builtin_nontemporal_store(floatx4{ov[0], ov[1], ov[2], ov[3]}, reinterpret_cast<floatx4 *>(o));
+                    else
+                        __builtin_nontemporal_store(floatx2{ov[0], ov[1]}, reinterpret_cast<floatx2 *>(o));
                 }
             }
         }
