@@ -550,3 +550,47 @@ def test_commit_multichunk_pipeline(B, T, F, Hkv, nvs):
     errs = dict(S=state_rel(S, Sr), Z=state_rel(Z[..., None], Zr[..., None]))
     report(f"multi-chunk commit B={B} T={T} F={F} Hkv={Hkv}", **errs)
     check(errs, dt)
+
+
+# ------------------------------- both sides of the small-batch split threshold
+@pytest.mark.parametrize("B", [8, 9])
+@pytest.mark.parametrize("F", [128, 64])
+def test_small_batch_split_threshold(B, F):
+    """bf16, d = 128, 16 heads: at B = 8 the (request, head) pairs fill half
+    of a 256-CU device and the step, the one-block commit and the fused step
+    + commit each run two workgroups per pair; at B = 9 one.  Both sides
+    against the oracle: a seeded prefix committed on both sides, then the
+    step, the commit of a ragged block (n_valid with 0) and the fused call on
+    a copy of the same states, through a slot map and with a gate."""
+    H, L, d, P = 16, 32, 128, 40
+    dt = torch.bfloat16
+    g = gen(9600 + 10 * B + F)
+    slots = B + 2
+    slot = torch.randperm(slots, generator=torch.Generator().manual_seed(B + F))[:B].to(torch.int32).to(DEV)
+    W = wl.feature_weights(H, d, F, dt, g, DEV)
+    pk, pv = wl.normal((B, H, P, d), 1, dt, g, DEV), wl.normal((B, H, P, d), 1, dt, g, DEV)
+    q, k, v = wl.block_qkv(B, H, L, d, dt, g, DEV)
+    gate = wl.gate_from_alpha(H, g, DEV)
+    n_valid = torch.tensor([(5 * b) % (L + 1) for b in range(B - 1)] + [L], dtype=torch.int32, device=DEV)
+    S0, Z0 = zeros_pool(slots, H, F, d)
+    S0 += 0.01 * torch.randn(S0.shape, generator=g, device=DEV)
+    Z0 += torch.rand(Z0.shape, generator=g, device=DEV)
+    S, Z = S0.clone(), Z0.clone()
+
+    hba.commit(pk, pv, W, S, Z, slot=slot)
+    Sp, Zp = oracle.commit(S0, Z0, pk, pv, W, slot=slot)
+    S2, Z2 = S.clone(), Z.clone()
+    out = hba.step(q, k, v, W, S, Z, gate=gate, slot=slot)
+    hba.commit(k, v, W, S, Z, n_valid=n_valid, slot=slot)
+    out_f = hba.step_commit(q, k, v, W, S2, Z2, gate=gate, slot=slot, n_valid=n_valid)
+
+    ref = oracle.step(q, k, v, W, Sp, Zp, gate=gate, slot=slot)
+    Sr, Zr = oracle.commit(Sp, Zp, k, v, W, n_valid=n_valid, slot=slot)
+    errs = dict(out=row_rel(out, ref), S=state_rel(S, Sr), Z=state_rel(Z[..., None], Zr[..., None]),
+                out_fused=row_rel(out_f, ref), S_fused=state_rel(S2, Sr), Z_fused=state_rel(Z2[..., None], Zr[..., None]))
+    report(f"split threshold B={B} F={F}", **errs)
+    check(errs, dt)
+    used = set(slot.tolist())
+    for s in range(slots):
+        if s not in used:
+            assert torch.equal(S[s], S0[s]) and torch.equal(S2[s], S0[s])
