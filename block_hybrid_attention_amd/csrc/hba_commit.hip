@@ -646,7 +646,10 @@ __global__ __launch_bounds__(128 * CW, CW == 2 ? 2 : 1) void commit_chunks_kerne
                 }
                 inv[r] = (16 * wave + 4 * lg + r) < nrows ? 1.0f / row16_sum(s0) : 0.f;
             }
-            float *phs = ph_of(j & 1) + li * G::PTLD + 16 * wave + 4 * lg;
+            // this lane's token quad 4 (wave%2) + lg of K-step wave/2, at chunk
+            // position q ^ (q/2 % 2) (see consume)
+            const int q = 4 * (wave & 1) + lg;
+            float *phs = ph_of(j & 1) + li * G::PTLD + 32 * (wave >> 1) + 4 * (q ^ ((q >> 1) & 1));
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
                 *reinterpret_cast<float4 *>(phs + 16 * nt * G::PTLD) =
@@ -717,15 +720,20 @@ __global__ __launch_bounds__(128 * CW, CW == 2 ? 2 : 1) void commit_chunks_kerne
         auto consume = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
             for (int kk = 0; kk < KC; ++kk) {
-                const float *phs = ph_of(j & 1) + (f_base + li) * G::PTLD + 32 * kk + 8 * lg;
+                // token quads 2 lg and 2 lg + 1 of K-step kk.  Quad q of a K-step
+                // sits at chunk position q ^ (q/2 % 2): with the 2-mod-4 row
+                // strides both these reads (lane quads 2 quads apart) and the
+                // producers' writes (1 apart) then fall on distinct banks.
+                const float *phs = ph_of(j & 1) + (f_base + li) * G::PTLD + 32 * kk;
+                const int p0 = 4 * ((2 * lg) ^ (lg & 1)), p1 = 4 * ((2 * lg + 1) ^ (lg & 1));
                 const T *vtb = vt_of(j & 1) + 32 * kk + 8 * lg;
                 bf16x8 bv[NE];
 #pragma unroll
                 for (int nt = 0; nt < NE; ++nt) bv[nt] = *reinterpret_cast<const bf16x8 *>(vtb + (16 * nt + li) * G::TP);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    const float4 x0 = *reinterpret_cast<const float4 *>(phs + 16 * mt * G::PTLD);
-                    const float4 x1 = *reinterpret_cast<const float4 *>(phs + 16 * mt * G::PTLD + 4);
+                    const float4 x0 = *reinterpret_cast<const float4 *>(phs + 16 * mt * G::PTLD + p0);
+                    const float4 x1 = *reinterpret_cast<const float4 *>(phs + 16 * mt * G::PTLD + p1);
                     const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
                     bf16x8 ah, al;
 #pragma unroll
