@@ -434,6 +434,29 @@ def test_deterministic_and_resumable():
     assert torch.equal(o1, o2) and torch.equal(o1, o3)
 
 
+
+@pytest.mark.parametrize("B,H", [(2, 4), (12, 16)])
+def test_fused_step_commit_deterministic(B, H):
+    """The fused step + commit, in both of its forms (two workgroups per pair
+    at 8 pairs; at 192 pairs one workgroup per pair whose two feature halves
+    add their partial sums in LDS), gives bitwise-equal outputs and states
+    from bitwise-equal inputs, over two consecutive blocks."""
+    L, d, F = 32, 128, 128
+    dt = torch.bfloat16
+    g = gen(8350 + B)
+    W = wl.feature_weights(H, d, F, dt, g, DEV)
+    S1, Z1 = zeros_pool(B, H, F, d)
+    S1 += 0.01 * torch.randn(S1.shape, generator=g, device=DEV)
+    Z1 += torch.rand(Z1.shape, generator=g, device=DEV)
+    S2, Z2 = S1.clone(), Z1.clone()
+    gate = wl.gate_from_alpha(H, g, DEV)
+    for _ in range(2):
+        q, k, v = wl.block_qkv(B, H, L, d, dt, g, DEV)
+        o1 = hba.step_commit(q, k, v, W, S1, Z1, gate=gate)
+        o2 = hba.step_commit(q, k, v, W, S2, Z2, gate=gate)
+        assert torch.equal(o1, o2)
+        assert torch.equal(S1, S2) and torch.equal(Z1, Z2)
+
 def test_int64_state_offsets():
     """A slot whose state starts past 2^31 fp32 elements of the pool."""
     H, d, F = 16, 128, 128
