@@ -508,8 +508,8 @@ def main():
                          "10 times, to calibrate HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the step shards by request with no exchange; see the design notes)", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the step shards by request, with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import torch
