@@ -443,11 +443,17 @@ __global__ __launch_bounds__(kThreads, 3) void step_kernel_bf16(StepArgs a) {
     const int c0 = part * (D / NSPLIT) + wave * NCOL + EPL * li;
     const float *s_lane = Sg + (int64_t)(8 * lg) * D + c0;
     float sreg[NCH][8][EPL];
+    // Non-temporal loads when the state streams from HBM at full rate (one
+    // workgroup per pair: 58.6-59.0 against 65.1-65.3 us at B = 128 with
+    // plain loads); plain loads in the latency-bound two-way split (8.65-8.7
+    // against 9.1 us at B = 8, 7.95 against 8.5 us at B = 4)
     auto load_chunk = [&](int c) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const float *p = s_lane + (int64_t)(32 * c + t) * D;
-            if constexpr (EPL == 2) {
+            if constexpr (NSPLIT == 2) {
+                sreg[c][t][0] = *p;
+            } else if constexpr (EPL == 2) {
                 const floatx2 v = __builtin_nontemporal_load(reinterpret_cast<const floatx2 *>(p));
                 sreg[c][t][0] = v[0];
                 sreg[c][t][1] = v[1];
