@@ -3,9 +3,9 @@ fp64 oracle.
 
 Each case draws, from its own seed, an input dtype, head_dim, feature width,
 query heads and a key/value head count dividing them, a batch (some large
-enough that the bf16 d = 128 step runs one workgroup per pair, most small
-enough for its column split; the last cases 24 to 48 requests at 8 to 16
-heads, more pairs than CUs), a block length in 1..32, a prefix of 0..100
+enough that the bf16 d = 128 kernels run one workgroup per pair, most small
+enough for their two-workgroup split; the last cases 24 to 48 requests at 8
+to 16 heads, more pairs than CUs), a block length in 1..32, a prefix of 0..100
 tokens committed in one call (one chunk or several), ragged n_valid with
 zeros, a slot map into a larger pool or none, a gate or none, and a ragged
 comparator prefix with a key split of 1, 2, 3 or 5.  Every case runs, on the
@@ -22,8 +22,8 @@ from parity import check, report, row_rel, state_rel
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-N_CASES = 40
-N_LARGE = 12   # cases N_CASES .. N_CASES + N_LARGE - 1: B = 24..48 at 8, 12 or 16 heads
+N_CASES = 60
+N_LARGE = 16   # cases N_CASES .. N_CASES + N_LARGE - 1: B = 24..48 at 8, 12 or 16 heads
 
 
 @pytest.fixture(scope="module", autouse=True)
